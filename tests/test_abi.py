@@ -1,0 +1,86 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/vpce.h declares, sizes its workspace independently of
+V, and rejects bad arguments before anything is enqueued (these calls make no
+HIP call at all)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import vocabulary_projection_cross_amd as vp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vpce.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vpce_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vp.library_path()):
+        pytest.fail("libvpce.so is not built (run __graft_entry__.build())")
+    return vp._load()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert names == ["vpce_backward", "vpce_forward", "vpce_status_string",
+                     "vpce_workspace_bytes"]
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {vp.library_path()}").read()
+    exported = set(re.findall(r" T (vpce_\w+)", out))
+    assert exported == set(names)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.vpce_status_string(s)
+    assert lib.vpce_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("N,d,R", [(65536, 7168, 8), (131072, 5120, 7),
+                                   (4096, 2048, 4), (1, 8, 1)])
+def test_workspace_independent_of_v(lib, N, d, R):
+    sizes = {lib.vpce_workspace_bytes(N, d, V, R, 0)
+             for V in (R, 32000, 129280, 151936, 1 << 30)}
+    assert len(sizes) == 1 and sizes.pop() > 0
+
+
+def test_workspace_rejects_bad_shapes(lib):
+    assert lib.vpce_workspace_bytes(10, 12, 100, 1, 0) == 0   # d % 8
+    assert lib.vpce_workspace_bytes(10, 12, 100, 1, 1) > 0    # f32: d % 4
+    assert lib.vpce_workspace_bytes(10, 16, 5, 6, 0) == 0     # R > V
+    assert lib.vpce_workspace_bytes(-1, 16, 5, 1, 0) == 0
+    assert lib.vpce_workspace_bytes(10, 16, 5, 1, 7) == 0     # dtype
+    assert lib.vpce_workspace_bytes(10, 16, 1 << 31, 1, 0) == 0
+    assert lib.vpce_workspace_bytes(0, 16, 5, 1, 0) > 0       # empty batch
+
+
+def _fwd(lib, H=8, W=16, lab=8, N=4, d=16, V=10, R=2, dt=0, loss=4, lse=4,
+         ws=256, wsb=1 << 20):
+    return lib.vpce_forward(H, W, lab, N, d, V, R, -100, dt, loss, lse, ws,
+                            wsb, None)
+
+
+def test_argument_errors_before_launch(lib):
+    A = 1 << 20   # aligned fake addresses: never dereferenced on error paths
+    assert _fwd(lib, H=A, W=A, lab=A, loss=A, lse=A, ws=A, dt=5) == 3
+    assert _fwd(lib, H=A, W=A, lab=A, loss=A, lse=A, ws=A, R=11) == 2
+    assert _fwd(lib, H=A, W=A, lab=A, loss=A, lse=A, ws=A, d=12) == 2
+    assert _fwd(lib, H=None, W=A, lab=A, loss=A, lse=A, ws=A) == 1
+    assert _fwd(lib, H=A, W=A, lab=A, loss=A, lse=A, ws=None) == 1
+    assert _fwd(lib, H=A + 8, W=A, lab=A, loss=A, lse=A, ws=A) == 4
+    assert _fwd(lib, H=A, W=A, lab=A, loss=A, lse=A, ws=A + 16) == 4
+    assert _fwd(lib, H=A, W=A, lab=A, loss=A, lse=A, ws=A, wsb=16) == 5
+    st = lib.vpce_backward(A, A, A, A, None, 4, 16, 10, 2, -100, 0, None, A,
+                           A, 1 << 20, None)
+    assert st == 1      # dH missing
+    st = lib.vpce_backward(A, A, A, A, None, 4, 16, 10, 2, -100, 0, A, A, A,
+                           16, None)
+    assert st == 5

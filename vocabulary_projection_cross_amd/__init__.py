@@ -1,0 +1,173 @@
+"""Blocked vocabulary-projection cross-entropy on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libvpce.so`` (declared in
+``include/vpce.h``). This module only marshals arguments: every step of the
+computation runs in the library's HIP kernels. PyTorch supplies device memory
+(so its allocator accounts for every byte, workspace included) and the current
+stream. There is no CPU path: if the library is missing, every call raises.
+
+    loss, lse = forward(H, W, labels, R)
+    dH, dW = backward(H, W, labels, lse, dloss, R)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["forward", "backward", "workspace_bytes", "VPCEError",
+           "library_path", "IGNORE_INDEX", "VPCE_BF16", "VPCE_F32"]
+
+IGNORE_INDEX = -100
+VPCE_BF16 = 0
+VPCE_F32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBPATH = os.path.join(_HERE, "libvpce.so")
+_lib = None
+
+
+class VPCEError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIBPATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIBPATH):
+        raise VPCEError(
+            "libvpce.so is not built; run "
+            "`python -m vocabulary_projection_cross_amd.build`")
+    lib = ctypes.CDLL(_LIBPATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, \
+        ctypes.c_size_t
+    lib.vpce_workspace_bytes.restype = sz
+    lib.vpce_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    lib.vpce_forward.restype = i32
+    lib.vpce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i32,
+                                 vp, vp, vp, sz, vp]
+    lib.vpce_backward.restype = i32
+    lib.vpce_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64,
+                                  i32, vp, vp, vp, sz, vp]
+    lib.vpce_status_string.restype = ctypes.c_char_p
+    lib.vpce_status_string.argtypes = [i32]
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return VPCE_BF16
+    if t == torch.float32:
+        return VPCE_F32
+    raise VPCEError(f"unsupported dtype {t}; expected bfloat16 or float32")
+
+
+def _check(status: int):
+    if status != 0:
+        msg = _load().vpce_status_string(status).decode()
+        raise VPCEError(f"vpce status {status}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _validate(H, W, labels):
+    for name, t in (("H", H), ("W", W), ("labels", labels)):
+        if not isinstance(t, torch.Tensor):
+            raise VPCEError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise VPCEError(f"{name} must be on a GPU device")
+        if not t.is_contiguous():
+            raise VPCEError(f"{name} must be contiguous")
+    if H.dim() != 2 or W.dim() != 2 or labels.dim() != 1:
+        raise VPCEError("expected H [N, d], W [V, d], labels [N]")
+    if H.shape[1] != W.shape[1] or labels.shape[0] != H.shape[0]:
+        raise VPCEError("shape mismatch between H, W and labels")
+    if H.dtype != W.dtype:
+        raise VPCEError("H and W must have the same dtype")
+    if labels.dtype != torch.int64:
+        raise VPCEError("labels must be int64")
+    if not (H.device == W.device == labels.device):
+        raise VPCEError("H, W and labels must be on the same device")
+
+
+def workspace_bytes(N: int, d: int, V: int, R: int,
+                    dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(_load().vpce_workspace_bytes(N, d, V, R, _dtype_code(dtype)))
+
+
+def _workspace(H, W, R, workspace):
+    need = workspace_bytes(H.shape[0], H.shape[1], W.shape[0], R, H.dtype)
+    if need == 0:
+        raise VPCEError("invalid shape for the vocabulary-projection CE")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise VPCEError(f"workspace too small: need {need} bytes")
+    return workspace
+
+
+def forward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, R: int,
+            ignore_index: int = IGNORE_INDEX,
+            workspace: Optional[torch.Tensor] = None
+            ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Mean cross-entropy of softmax(H W^T) against labels, computed shard by
+    shard with an online log-sum-exp. Returns (loss [] fp32, lse [N] fp32)."""
+    _validate(H, W, labels)
+    lib = _load()
+    N, d = H.shape
+    V = W.shape[0]
+    ws = _workspace(H, W, R, workspace)
+    loss = torch.empty((), dtype=torch.float32, device=H.device)
+    lse = torch.empty(N, dtype=torch.float32, device=H.device)
+    stream = torch.cuda.current_stream(H.device).cuda_stream
+    with torch.cuda.device(H.device):
+        st = lib.vpce_forward(_ptr(H), _ptr(W), _ptr(labels), N, d, V, R,
+                              ignore_index, _dtype_code(H.dtype), _ptr(loss),
+                              _ptr(lse), _ptr(ws), ws.numel(),
+                              ctypes.c_void_p(stream))
+    _check(st)
+    return loss, lse
+
+
+def backward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+             lse: torch.Tensor, dloss: Optional[torch.Tensor], R: int,
+             ignore_index: int = IGNORE_INDEX,
+             workspace: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gradients of the mean loss times dloss (a device scalar; None = 1).
+    Returns (dH [N, d] fp32, dW [V, d] fp32)."""
+    _validate(H, W, labels)
+    lib = _load()
+    N, d = H.shape
+    V = W.shape[0]
+    if (lse.device != H.device or lse.dtype != torch.float32
+            or lse.numel() != N or not lse.is_contiguous()):
+        raise VPCEError("lse must be a contiguous fp32 [N] tensor on H's "
+                        "device")
+    if dloss is not None:
+        if (dloss.device != H.device or dloss.dtype != torch.float32
+                or dloss.numel() != 1):
+            raise VPCEError("dloss must be a one-element fp32 tensor on H's "
+                            "device")
+        dloss = dloss.contiguous()
+    ws = _workspace(H, W, R, workspace)
+    dH = torch.empty((N, d), dtype=torch.float32, device=H.device)
+    dW = torch.empty((V, d), dtype=torch.float32, device=H.device)
+    stream = torch.cuda.current_stream(H.device).cuda_stream
+    with torch.cuda.device(H.device):
+        st = lib.vpce_backward(_ptr(H), _ptr(W), _ptr(labels), _ptr(lse),
+                               _ptr(dloss), N, d, V, R, ignore_index,
+                               _dtype_code(H.dtype), _ptr(dH), _ptr(dW),
+                               _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    _check(st)
+    return dH, dW

@@ -1,0 +1,725 @@
+// vpce.hip -- kernels and C ABI of the blocked vocabulary-projection
+// cross-entropy for gfx950 ("Flattening Every Memory Peak in Long-Context
+// Mixture-of-Experts Training", section 3.2 "Ring-DTP", Figure 3).
+//
+// Forward: the R vocabulary shards are the rounds of the ring. A workgroup
+// owns one 256-token tile, one shard and one contiguous split of that shard's
+// 256-column vocabulary tiles. For each vocabulary tile it forms the logit
+// tile with MFMA (never leaving registers), folds it into a per-token running
+// (max, sum-exp) state with the online-softmax update, and picks up the target
+// logit if the tile owns the label. At the end of the split the state is
+// written as one partial per token. A merge kernel folds the partials of all
+// shards in ring order, giving the per-token log-sum-exp, the per-token NLL and
+// the mean loss (fp64 accumulation, fixed order).
+//
+// Backward: the shards are replayed in the same order, each in fixed-width
+// chunks of C columns. Per chunk: recompute the logit tile, form
+// G = dloss/n * (exp(z - lse) - onehot) in registers and store it (bf16 or
+// fp32) both token-major and vocabulary-major; then dW_chunk = G^T H and
+// dH += G W_chunk, both on the same MFMA tile engine. Transposed copies of H
+// (once) and of the W chunk (per chunk) make every contraction an NT product.
+// Device working set: partials R x S x N, the G chunk N x C twice, H^T and the
+// W^T chunk -- fixed by N, d, R, S and C, never by V.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "tile_core.hpp"
+#include "vpce.h"
+
+using namespace vpce;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kChunkCols = 4096;  // backward chunk width C
+constexpr int kMaxSplits = 16;
+constexpr int64_t kMaxTokens = 2000000;
+constexpr int kGroupM = 4;
+constexpr int kLabIgnored = -2;   // label slot codes in LDS
+constexpr int kLabInvalid = -1;
+
+struct Shards {
+  int64_t V;
+  int R;
+  __host__ __device__ int64_t begin(int r) const {
+    const int64_t base = V / R, extra = V % R;
+    return r * base + (r < extra ? r : extra);
+  }
+  __host__ __device__ int64_t width(int r) const {
+    const int64_t base = V / R, extra = V % R;
+    return base + (r < extra ? 1 : 0);
+  }
+};
+
+__device__ __forceinline__ int label_code(int64_t y, int64_t ignore_index,
+                                          int64_t V) {
+  if (y == ignore_index) return kLabIgnored;
+  if (y < 0 || y >= V) return kLabInvalid;
+  return (int)y;
+}
+
+__device__ __forceinline__ int clamp_rows(int64_t remaining) {
+  return remaining <= 0 ? 0 : (remaining >= kTile ? kTile : (int)remaining);
+}
+
+// ---------------------------------------------------------------------------
+// Forward tile kernel
+// ---------------------------------------------------------------------------
+struct FwdParams {
+  const void* H;
+  const void* W;
+  const int64_t* labels;
+  int64_t N, d, V, ignore_index;
+  int R, S, T;  // shards, splits per shard, token tiles
+  float* part_m;  // [R*S][N], base-2 running max
+  float* part_s;  // [R*S][N], running sum of 2^(y - m)
+  float* tgt;     // [N] target logit (natural units)
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_lse_kernel(FwdParams a) {
+  __shared__ __attribute__((aligned(16))) char smem[kGemmLds];
+  __shared__ __attribute__((aligned(16))) int lab_s[kTile];
+  __shared__ float xm[2][256], xs[2][256];
+
+  const int total = a.T * a.R * a.S;
+  const int idx = xcd_remap(blockIdx.x, total);
+  int it, g;
+  grouped_tile(idx, a.T, a.R * a.S, kGroupM, it, g);
+  const int r = g / a.S, j = g % a.S;
+  const Shards sh{a.V, a.R};
+  const int64_t v0 = sh.begin(r), vw = sh.width(r);
+  const int64_t vend = v0 + vw;
+  const int Q = (int)((vw + kTile - 1) / kTile);
+  const int q0 = (int)((int64_t)Q * j / a.S), q1 = (int)((int64_t)Q * (j + 1) / a.S);
+
+  const int tid = threadIdx.x;
+  const int64_t tok0 = (int64_t)it * kTile;
+  {
+    const int64_t tok = tok0 + tid;
+    lab_s[tid] = tok < a.N ? label_code(a.labels[tok], a.ignore_index, a.V)
+                           : kLabIgnored;
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int p = lane & 31, h = lane >> 5;
+
+  const T* Hb = reinterpret_cast<const T*>(a.H) + tok0 * a.d;
+  const int a_rows = clamp_rows(a.N - tok0);
+
+  // running (max, sum) in base-2 units for row slot p>>1 of each 32-row block
+  float run_m[4], run_s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { run_m[i] = -INFINITY; run_s[i] = 0.f; }
+  f32x16_t acc[4][4];
+
+  for (int q = q0; q < q1; ++q) {
+    const int64_t col0 = v0 + (int64_t)q * kTile;
+    const T* Wb = reinterpret_cast<const T*>(a.W) + col0 * a.d;
+    tile_mainloop<T>(acc, Hb, a.d, a_rows, Wb, a.d, clamp_rows(vend - col0),
+                     a.d, smem);
+    // columns of this lane: lc + 32*jj, jj = 0..3 (global vocabulary index)
+    const int64_t lc = col0 + wn * 128 + p;
+    bool cv[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) cv[jj] = lc + jj * 32 < vend;
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float ml[16], sl[16];
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        // 4 consecutive rows: 8*rq + 4*h + (0..3) within the 32-row block
+        const int rowb = wm * 128 + i * 32 + 8 * rq + 4 * h;
+        const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = rq * 4 + e;
+          float y[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            y[jj] = cv[jj] ? acc[i][jj][rr] * kLog2e : -INFINITY;
+          const float m = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+          float s = 0.f;
+          if (cv[0]) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) s += fast_exp2(y[jj] - m);
+          }
+          ml[rr] = m;
+          sl[rr] = s;
+          // target logit: the label's column is lc + 32*jj for some jj
+          const int lab = e == 0 ? labs.x : e == 1 ? labs.y : e == 2 ? labs.z : labs.w;
+          const int64_t off = (int64_t)lab - lc;
+          if (lab >= 0 && off >= 0 && off < 128 && (off & 31) == 0 &&
+              (int64_t)lab < vend) {
+            const int jj = (int)(off >> 5);
+            const float z = jj == 0 ? acc[i][0][rr] : jj == 1 ? acc[i][1][rr]
+                          : jj == 2 ? acc[i][2][rr] : acc[i][3][rr];
+            a.tgt[tok0 + rowb + e] = z;
+          }
+        }
+      }
+      // reduce-scatter the 16 row states across the 32 lanes of each half;
+      // afterwards lanes p and p^1 both hold row slot p>>1, fully reduced.
+#define VPCE_RS_STEP(MASK, HALF)                                        \
+      {                                                                 \
+        const bool upper = (p & (MASK)) != 0;                           \
+        _Pragma("unroll") for (int k = 0; k < (HALF); ++k) {            \
+          const float mk = upper ? ml[k + (HALF)] : ml[k];              \
+          const float sk = upper ? sl[k + (HALF)] : sl[k];              \
+          const float mo = half_xor<MASK>(upper ? ml[k] : ml[k + (HALF)]); \
+          const float so = half_xor<MASK>(upper ? sl[k] : sl[k + (HALF)]); \
+          float m = mk, s = sk;                                         \
+          ms_merge(m, s, mo, so);                                       \
+          ml[k] = m;                                                    \
+          sl[k] = s;                                                    \
+        }                                                               \
+      }
+      VPCE_RS_STEP(16, 8)
+      VPCE_RS_STEP(8, 4)
+      VPCE_RS_STEP(4, 2)
+      VPCE_RS_STEP(2, 1)
+#undef VPCE_RS_STEP
+      {
+        const float mo = half_xor<1>(ml[0]);
+        const float so = half_xor<1>(sl[0]);
+        ms_merge(ml[0], sl[0], mo, so);
+      }
+      ms_merge(run_m[i], run_s[i], ml[0], sl[0]);
+    }
+  }
+
+  // the two waves sharing rows (wn = 0, 1) combine through LDS
+  if (wn == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xm[wm][i * 64 + lane] = run_m[i];
+      xs[wm][i * 64 + lane] = run_s[i];
+    }
+  }
+  __syncthreads();
+  if (wn == 0 && (p & 1) == 0) {
+    const int rr = p >> 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = run_m[i], s = run_s[i];
+      ms_merge(m, s, xm[wm][i * 64 + lane], xs[wm][i * 64 + lane]);
+      const int row = wm * 128 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+      const int64_t tok = tok0 + row;
+      if (tok < a.N) {
+        const int64_t o = (int64_t)(r * a.S + j) * a.N + tok;
+        a.part_m[o] = m;
+        a.part_s[o] = s;
+      }
+    }
+  }
+}
+
+__global__ void fill_kernel(float* x, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = v;
+}
+
+// Fold the partials of every shard (ring order) and split; write lse and the
+// per-block sums of the token losses (fp64) and valid counts.
+__global__ __launch_bounds__(256) void merge_kernel(
+    const float* part_m, const float* part_s, const float* tgt,
+    const int64_t* labels, int64_t N, int G, int64_t ignore_index,
+    float* lse, double* bsum, int* bcnt) {
+  __shared__ double ssum[256];
+  __shared__ int scnt[256];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  double nll = 0.0;
+  int cnt = 0;
+  if (i < N) {
+    float m = -INFINITY, s = 0.f;
+    for (int gg = 0; gg < G; ++gg)
+      ms_merge(m, s, part_m[(int64_t)gg * N + i], part_s[(int64_t)gg * N + i]);
+    const float l = (m + __builtin_amdgcn_logf(s)) * kLn2;
+    lse[i] = l;
+    if (labels[i] != ignore_index) {
+      nll = (double)l - (double)tgt[i];
+      cnt = 1;
+    }
+  }
+  ssum[threadIdx.x] = nll;
+  scnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      ssum[threadIdx.x] += ssum[threadIdx.x + w];
+      scnt[threadIdx.x] += scnt[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    bsum[blockIdx.x] = ssum[0];
+    bcnt[blockIdx.x] = scnt[0];
+  }
+}
+
+__global__ __launch_bounds__(256) void loss_kernel(const double* bsum,
+                                                   const int* bcnt, int nb,
+                                                   float* loss) {
+  __shared__ double ssum[256];
+  __shared__ long long scnt[256];
+  double s = 0.0;
+  long long c = 0;
+  for (int b = threadIdx.x; b < nb; b += 256) {
+    s += bsum[b];
+    c += bcnt[b];
+  }
+  ssum[threadIdx.x] = s;
+  scnt[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      ssum[threadIdx.x] += ssum[threadIdx.x + w];
+      scnt[threadIdx.x] += scnt[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0)
+    loss[0] = scnt[0] > 0 ? (float)(ssum[0] / (double)scnt[0]) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Backward kernels
+// ---------------------------------------------------------------------------
+
+// scale = dloss / n_valid (0 when no token counts)
+__global__ __launch_bounds__(1024) void scale_kernel(const int64_t* labels,
+                                                     int64_t N,
+                                                     int64_t ignore_index,
+                                                     const float* dloss,
+                                                     float* scale) {
+  __shared__ long long sc[1024];
+  long long c = 0;
+  for (int64_t i = threadIdx.x; i < N; i += 1024) c += labels[i] != ignore_index;
+  sc[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) sc[threadIdx.x] += sc[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float up = dloss ? dloss[0] : 1.f;
+    scale[0] = sc[0] > 0 ? (float)((double)up / (double)sc[0]) : 0.f;
+  }
+}
+
+// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < dst_cols; c < cols.
+// Element type U is the raw storage (uint16_t for bf16, uint32_t for fp32).
+template <typename U>
+__global__ __launch_bounds__(256) void transpose_kernel(
+    const U* __restrict__ src, int64_t ld_src, int64_t rows, int64_t cols,
+    U* __restrict__ dst, int64_t ld_dst, int64_t dst_cols) {
+  __shared__ U t[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t r = r0 + k, c = c0 + tx;
+    U v = 0;
+    if (r < rows && c < cols) v = src[r * ld_src + c];
+    t[k][tx] = v;
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t c = c0 + k, r = r0 + tx;
+    if (c < cols && r < dst_cols) dst[c * ld_dst + r] = t[tx][k];
+  }
+}
+
+struct GParams {
+  const void* H;
+  const void* Wc;        // first row of the chunk in W
+  const int64_t* labels;
+  const float* lse;
+  const float* scale;
+  int64_t N, N_pad, d, V, ignore_index;
+  int64_t cv0;           // global vocabulary index of chunk column 0
+  int64_t C_eff, C_pad;  // valid / padded chunk width
+  int T, CT;             // token tiles, chunk column tiles
+  void* G;               // [N][C_pad]
+  void* GT;              // [C_pad][N_pad]
+};
+
+__device__ __forceinline__ void store_elem(__bf16* p, float v) { *p = (__bf16)v; }
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c,
+                                       float d) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+  *reinterpret_cast<bf16x4_t*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c,
+                                       float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void recompute_g_kernel(GParams a) {
+  __shared__ __attribute__((aligned(16))) char smem[kGemmLds];
+  __shared__ __attribute__((aligned(16))) int lab_s[kTile];
+  __shared__ __attribute__((aligned(16))) float lse_s[kTile];
+
+  const int total = a.T * a.CT;
+  const int idx = xcd_remap(blockIdx.x, total);
+  int it, ct;
+  grouped_tile(idx, a.T, a.CT, kGroupM, it, ct);
+  const int tid = threadIdx.x;
+  const int64_t tok0 = (int64_t)it * kTile;
+  const int64_t c0 = (int64_t)ct * kTile;
+  {
+    const int64_t tok = tok0 + tid;
+    lab_s[tid] = tok < a.N ? label_code(a.labels[tok], a.ignore_index, a.V)
+                           : kLabIgnored;
+    lse_s[tid] = tok < a.N ? a.lse[tok] * kLog2e : 0.f;
+  }
+  f32x16_t acc[4][4];
+  tile_mainloop<T>(acc, reinterpret_cast<const T*>(a.H) + tok0 * a.d, a.d,
+                   clamp_rows(a.N - tok0),
+                   reinterpret_cast<const T*>(a.Wc) + c0 * a.d, a.d,
+                   clamp_rows(a.C_eff - c0), a.d, smem);
+  const float scale = a.scale[0];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int p = lane & 31, h = lane >> 5;
+  T* G = reinterpret_cast<T*>(a.G);
+  T* GT = reinterpret_cast<T*>(a.GT);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int64_t c = c0 + wn * 128 + jj * 32 + p;  // chunk column
+    const bool cvalid = c < a.C_eff;
+    const bool cstore = c < a.C_pad;
+    const int v = (int)(a.cv0 + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int rowb = wm * 128 + i * 32 + 8 * rq + 4 * h;
+        const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
+        const float4 l2 = *reinterpret_cast<const float4*>(&lse_s[rowb]);
+        float gv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int lab = e == 0 ? labs.x : e == 1 ? labs.y : e == 2 ? labs.z : labs.w;
+          const float ls = e == 0 ? l2.x : e == 1 ? l2.y : e == 2 ? l2.z : l2.w;
+          const float z = acc[i][jj][rq * 4 + e];
+          float gg = 0.f;
+          if (cvalid && lab != kLabIgnored) {
+            const float pr = fast_exp2(fmaf(z, kLog2e, -ls));
+            gg = scale * (pr - (lab == v ? 1.f : 0.f));
+          }
+          gv[e] = gg;
+          const int64_t tok = tok0 + rowb + e;
+          if (cstore && tok < a.N) store_elem(G + tok * a.C_pad + c, gg);
+        }
+        const int64_t tokb = tok0 + rowb;
+        if (cstore && tokb < a.N_pad)
+          store4(GT + c * a.N_pad + tokb, gv[0], gv[1], gv[2], gv[3]);
+      }
+    }
+  }
+}
+
+// out[M x Nc] (row stride ldo) = A . B^T over K, stored or accumulated (fp32).
+struct ProdParams {
+  const void* A;
+  int64_t lda;
+  int64_t M;
+  const void* B;
+  int64_t ldb;
+  int64_t Nc;
+  int64_t K;
+  float* out;
+  int64_t ldo;
+  int TM, TN;
+  int accumulate;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prod_kernel(ProdParams a) {
+  __shared__ __attribute__((aligned(16))) char smem[kGemmLds];
+  const int total = a.TM * a.TN;
+  const int idx = xcd_remap(blockIdx.x, total);
+  int tm, tn;
+  grouped_tile(idx, a.TM, a.TN, kGroupM, tm, tn);
+  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+  f32x16_t acc[4][4];
+  tile_mainloop<T>(acc, reinterpret_cast<const T*>(a.A) + m0 * a.lda, a.lda,
+                   clamp_rows(a.M - m0),
+                   reinterpret_cast<const T*>(a.B) + n0 * a.ldb, a.ldb,
+                   clamp_rows(a.Nc - n0), a.K, smem);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int p = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int64_t col = n0 + wn * 128 + jj * 32 + p;
+    if (col >= a.Nc) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        if (row < a.M) {
+          float* o = a.out + row * a.ldo + col;
+          const float v = acc[i][jj][rr];
+          *o = a.accumulate ? *o + v : v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation, plan, launches
+// ---------------------------------------------------------------------------
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  int64_t N, d, V;
+  int R, dt, esz;
+  int T, S, nb;
+  int64_t N_pad, C;
+  // forward layout
+  size_t o_pm, o_ps, o_tgt, o_bsum, o_bcnt, fwd_bytes;
+  // backward layout
+  size_t o_scale, o_HT, o_G, o_GT, o_WT, bwd_bytes;
+  size_t bytes;
+};
+
+int splits_for(int64_t T, int R) {
+  // enough workgroups to cover the 256 compute units twice, never
+  // depending on V
+  const int64_t want = 512;
+  int64_t s = (want + T * R - 1) / (T * R);
+  if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return (int)s;
+}
+
+int32_t check_shape(int64_t N, int64_t d, int64_t V, int32_t R, int32_t dt) {
+  if (dt != VPCE_BF16 && dt != VPCE_F32) return VPCE_ERR_UNSUPPORTED;
+  if (N < 0 || d < 1 || V < 1 || R < 1 || (int64_t)R > V) return VPCE_ERR_SHAPE;
+  // 32-bit buffer offsets: 256 rows of any operand (H^T rows are N long)
+  // stay below 2^31 bytes
+  if (V >= ((int64_t)1 << 31) || N > kMaxTokens || d > kMaxTokens)
+    return VPCE_ERR_SHAPE;
+  if (d % (dt == VPCE_BF16 ? 8 : 4) != 0) return VPCE_ERR_SHAPE;
+  // tile indices are int: keep the grids in range
+  if ((N + kTile - 1) / kTile * (int64_t)R * kMaxSplits >= ((int64_t)1 << 31))
+    return VPCE_ERR_SHAPE;
+  return VPCE_OK;
+}
+
+Plan make_plan(int64_t N, int64_t d, int64_t V, int R, int dt) {
+  Plan p{};
+  p.N = N; p.d = d; p.V = V; p.R = R; p.dt = dt;
+  p.esz = dt == VPCE_BF16 ? 2 : 4;
+  p.T = (int)((N + kTile - 1) / kTile);
+  p.S = splits_for(p.T > 0 ? p.T : 1, R);
+  p.nb = (int)((N + 255) / 256);
+  p.N_pad = (N + 63) / 64 * 64;
+  p.C = kChunkCols;
+  size_t o = 0;
+  const size_t part = (size_t)R * p.S * (size_t)N * 4;
+  p.o_pm = o; o = up(o + part);
+  p.o_ps = o; o = up(o + part);
+  p.o_tgt = o; o = up(o + (size_t)N * 4);
+  p.o_bsum = o; o = up(o + (size_t)(p.nb > 0 ? p.nb : 1) * 8);
+  p.o_bcnt = o; o = up(o + (size_t)(p.nb > 0 ? p.nb : 1) * 4);
+  p.fwd_bytes = o;
+  o = 0;
+  p.o_scale = o; o = up(o + 16);
+  p.o_HT = o; o = up(o + (size_t)d * p.N_pad * p.esz);
+  p.o_G = o; o = up(o + (size_t)N * p.C * p.esz);
+  p.o_GT = o; o = up(o + (size_t)p.C * p.N_pad * p.esz);
+  p.o_WT = o; o = up(o + (size_t)d * p.C * p.esz);
+  p.bwd_bytes = o;
+  p.bytes = p.fwd_bytes > p.bwd_bytes ? p.fwd_bytes : p.bwd_bytes;
+  return p;
+}
+
+inline bool aligned(const void* p, size_t a) {
+  return ((uintptr_t)p % a) == 0;
+}
+
+#define VPCE_LAUNCH_CHECK()                              \
+  do {                                                   \
+    if (hipGetLastError() != hipSuccess) return VPCE_ERR_HIP; \
+  } while (0)
+
+template <typename T>
+int32_t run_forward(const Plan& p, const void* H, const void* W,
+                    const int64_t* labels, int64_t ignore_index, float* loss,
+                    float* lse, char* ws, hipStream_t st) {
+  float* pm = reinterpret_cast<float*>(ws + p.o_pm);
+  float* ps = reinterpret_cast<float*>(ws + p.o_ps);
+  float* tgt = reinterpret_cast<float*>(ws + p.o_tgt);
+  double* bsum = reinterpret_cast<double*>(ws + p.o_bsum);
+  int* bcnt = reinterpret_cast<int*>(ws + p.o_bcnt);
+  if (p.N > 0) {
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0, st,
+                       tgt, p.N, NAN);
+    VPCE_LAUNCH_CHECK();
+    FwdParams fp{H, W, labels, p.N, p.d, p.V, ignore_index, p.R, p.S, p.T, pm, ps, tgt};
+    const unsigned grid = (unsigned)((int64_t)p.T * p.R * p.S);
+    hipLaunchKernelGGL(fwd_lse_kernel<T>, dim3(grid), dim3(kThreads), 0, st, fp);
+    VPCE_LAUNCH_CHECK();
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)p.nb), dim3(256), 0, st, pm, ps,
+                       tgt, labels, p.N, p.R * p.S, ignore_index, lse, bsum, bcnt);
+    VPCE_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsum, bcnt, p.nb, loss);
+  VPCE_LAUNCH_CHECK();
+  return VPCE_OK;
+}
+
+template <typename T, typename U>
+int32_t run_backward(const Plan& p, const void* H, const void* W,
+                     const int64_t* labels, const float* lse,
+                     const float* dloss, int64_t ignore_index, float* dH,
+                     float* dW, char* ws, hipStream_t st) {
+  float* scale = reinterpret_cast<float*>(ws + p.o_scale);
+  void* HT = ws + p.o_HT;
+  void* G = ws + p.o_G;
+  void* GT = ws + p.o_GT;
+  void* WT = ws + p.o_WT;
+  hipLaunchKernelGGL(scale_kernel, dim3(1), dim3(1024), 0, st, labels, p.N,
+                     ignore_index, dloss, scale);
+  VPCE_LAUNCH_CHECK();
+  if (p.N_pad > 0) {
+    // H^T [d][N_pad], zero in the padding columns
+    dim3 g((unsigned)((p.N_pad + 63) / 64), (unsigned)((p.d + 63) / 64));
+    hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st,
+                       reinterpret_cast<const U*>(H), p.d, p.N, p.d,
+                       reinterpret_cast<U*>(HT), p.N_pad, p.N_pad);
+    VPCE_LAUNCH_CHECK();
+  }
+  const Shards sh{p.V, p.R};
+  const int TD = (int)((p.d + kTile - 1) / kTile);
+  bool first = true;
+  for (int r = 0; r < p.R; ++r) {
+    const int64_t v0 = sh.begin(r), vw = sh.width(r);
+    for (int64_t c0 = 0; c0 < vw; c0 += p.C) {
+      const int64_t ceff = (vw - c0) < p.C ? (vw - c0) : p.C;
+      const int64_t cpad = (ceff + 63) / 64 * 64;
+      const int64_t cv0 = v0 + c0;
+      const U* Wc = reinterpret_cast<const U*>(W) + cv0 * p.d;
+      // W^T chunk [d][C_pad], zero in the padding columns
+      {
+        dim3 g((unsigned)((cpad + 63) / 64), (unsigned)((p.d + 63) / 64));
+        hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st, Wc, p.d, ceff,
+                           p.d, reinterpret_cast<U*>(WT), cpad, cpad);
+        VPCE_LAUNCH_CHECK();
+      }
+      const int CT = (int)((cpad + kTile - 1) / kTile);
+      if (p.N > 0) {
+        GParams gp{H, Wc, labels, lse, scale, p.N, p.N_pad, p.d, p.V,
+                   ignore_index, cv0, ceff, cpad, p.T, CT, G, GT};
+        hipLaunchKernelGGL(recompute_g_kernel<T>, dim3((unsigned)(p.T * CT)),
+                           dim3(kThreads), 0, st, gp);
+        VPCE_LAUNCH_CHECK();
+      }
+      // dW rows [cv0, cv0 + ceff) = G^T H : A = G^T [C_pad x N_pad], B = H^T
+      {
+        const int TM = (int)((ceff + kTile - 1) / kTile);
+        ProdParams pp{GT, p.N_pad, ceff, HT, p.N_pad, p.d, p.N_pad,
+                      dW + cv0 * p.d, p.d, TM, TD, 0};
+        hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(TM * TD)), dim3(kThreads), 0,
+                           st, pp);
+        VPCE_LAUNCH_CHECK();
+      }
+      // dH (+)= G W_chunk : A = G [N x C_pad], B = W^T chunk [d x C_pad]
+      if (p.N > 0) {
+        ProdParams pp{G, cpad, p.N, WT, cpad, p.d, cpad, dH, p.d, p.T, TD,
+                      first ? 0 : 1};
+        hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(p.T * TD)), dim3(kThreads), 0,
+                           st, pp);
+        VPCE_LAUNCH_CHECK();
+      }
+      first = false;
+    }
+  }
+  return VPCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t vpce_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
+                            int32_t dtype) {
+  if (check_shape(N, d, V, R, dtype) != VPCE_OK) return 0;
+  return make_plan(N, d, V, R, dtype).bytes;
+}
+
+int32_t vpce_forward(const void* H, const void* W, const int64_t* labels,
+                     int64_t N, int64_t d, int64_t V, int32_t R,
+                     int64_t ignore_index, int32_t dtype, float* loss,
+                     float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  const int32_t s = check_shape(N, d, V, R, dtype);
+  if (s != VPCE_OK) return s;
+  if (!W || !loss || !workspace) return VPCE_ERR_NULL;
+  if (N > 0 && (!H || !labels || !lse)) return VPCE_ERR_NULL;
+  if ((H && !aligned(H, 16)) || !aligned(W, 16) || (labels && !aligned(labels, 8)) ||
+      !aligned(loss, 4) || (lse && !aligned(lse, 4)) || !aligned(workspace, kAlign))
+    return VPCE_ERR_ALIGN;
+  const Plan p = make_plan(N, d, V, R, dtype);
+  if (workspace_bytes < p.bytes) return VPCE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == VPCE_BF16)
+    return run_forward<__bf16>(p, H, W, labels, ignore_index, loss, lse, ws, st);
+  return run_forward<float>(p, H, W, labels, ignore_index, loss, lse, ws, st);
+}
+
+int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
+                      const float* lse, const float* dloss, int64_t N,
+                      int64_t d, int64_t V, int32_t R, int64_t ignore_index,
+                      int32_t dtype, float* dH, float* dW, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const int32_t s = check_shape(N, d, V, R, dtype);
+  if (s != VPCE_OK) return s;
+  if (!W || !dW || !workspace) return VPCE_ERR_NULL;
+  if (N > 0 && (!H || !labels || !lse || !dH)) return VPCE_ERR_NULL;
+  if ((H && !aligned(H, 16)) || !aligned(W, 16) || (labels && !aligned(labels, 8)) ||
+      (lse && !aligned(lse, 4)) || (dloss && !aligned(dloss, 4)) ||
+      (dH && !aligned(dH, 4)) || !aligned(dW, 4) || !aligned(workspace, kAlign))
+    return VPCE_ERR_ALIGN;
+  const Plan p = make_plan(N, d, V, R, dtype);
+  if (workspace_bytes < p.bytes) return VPCE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == VPCE_BF16)
+    return run_backward<__bf16, uint16_t>(p, H, W, labels, lse, dloss,
+                                          ignore_index, dH, dW, ws, st);
+  return run_backward<float, uint32_t>(p, H, W, labels, lse, dloss,
+                                       ignore_index, dH, dW, ws, st);
+}
+
+const char* vpce_status_string(int32_t status) {
+  switch (status) {
+    case VPCE_OK: return "ok";
+    case VPCE_ERR_NULL: return "a required pointer is NULL";
+    case VPCE_ERR_SHAPE: return "invalid shape (N, d, V or R)";
+    case VPCE_ERR_UNSUPPORTED: return "unsupported dtype";
+    case VPCE_ERR_ALIGN: return "misaligned pointer";
+    case VPCE_ERR_WORKSPACE: return "workspace too small";
+    case VPCE_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"
