@@ -87,6 +87,30 @@ __device__ __forceinline__ void mma_block(f32x16_t (&acc)[4][4],
                                                          acc[i][j], 0, 0, 0);
 }
 
+// One accumulator row block (4 accumulators sharing the A fragment).
+__device__ __forceinline__ void mma_row(f32x16_t (&acc)[4], u32x4_t a,
+                                        const u32x4_t (&b)[4],
+                                        const __bf16*) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[j]),
+        acc[j], 0, 0, 0);
+}
+__device__ __forceinline__ void mma_row(f32x16_t (&acc)[4], u32x4_t a,
+                                        const u32x4_t (&b)[4], const float*) {
+  const f32x4_t af = __builtin_bit_cast(f32x4_t, a);
+  f32x4_t bf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bf[j] = __builtin_bit_cast(f32x4_t, b[j]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[j][e], acc[j],
+                                                    0, 0, 0);
+}
+
 // A buffer resource over the valid rows of one operand tile: loads past its
 // end return zero, which masks ragged row tails without branches.
 template <typename T>
@@ -168,30 +192,80 @@ __device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[4][4],
   stage_store(smem + 2 * kStageBytes, rb);
   __syncthreads();
   const T* tag = nullptr;
+  // Software pipeline, per stage of 4 chunk-pair steps:
+  //   step 0: issue the next stage's global loads; read step 1's fragments
+  //   steps 1, 2: read the following step's fragments
+  //   step 3: write the next stage into the other LDS buffer
+  // each while the MFMAs of the current step run; then one barrier and the
+  // next stage's step-0 fragments. Past the last stage the loads fall
+  // outside the resource (zeros) and land in the idle buffer.
+  u32x4_t fa[2][4], fb[2][4];
+  const int arow = wm * 128 + p, brow = wn * 128 + p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[0][i] = frag(smem, arow + i * 32, h);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[0][j] = frag(smem + 2 * kStageBytes, brow + j * 32, h);
+  constexpr int E = Chunk<T>::E;
+  const int t = threadIdx.x;
+  const uint32_t rowa = (uint32_t)(lda * (int64_t)sizeof(T));
+  const uint32_t rowbb = (uint32_t)(ldb * (int64_t)sizeof(T));
+  const uint32_t base_a = (uint32_t)(t >> 3) * rowa + (uint32_t)((t & 7) * E * sizeof(T));
+  const uint32_t base_b = (uint32_t)(t >> 3) * rowbb + (uint32_t)((t & 7) * E * sizeof(T));
+  const int st_off = lds_off(t >> 3, t & 7);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      stage_load<T>(ra, rsa, lda, (int64_t)(kt + 1) * BK, K);
-      stage_load<T>(rb, rsb, ldb, (int64_t)(kt + 1) * BK, K);
-    }
     const char* sa = smem + cur * kStageBytes;
     const char* sb = smem + (2 + cur) * kStageBytes;
+    char* wa = smem + (cur ^ 1) * kStageBytes + st_off;
+    char* wb = smem + (2 + (cur ^ 1)) * kStageBytes + st_off;
+    // next stage's global offsets (past K: outside the resource -> zeros)
+    const int64_t kn = (int64_t)(kt + 1) * BK + (t & 7) * E;
+    const bool kin = kn < K;
+    const uint32_t ga = kin ? base_a + (uint32_t)((kt + 1) * BK * sizeof(T)) : 0x80000000u;
+    const uint32_t gb = kin ? base_b + (uint32_t)((kt + 1) * BK * sizeof(T)) : 0x80000000u;
+    // The stage is issued as 16 groups of 4 MFMAs; sched_barrier keeps
+    // each group's memory operations next to its MFMAs:
+    //   steps 0-2, group q: read fragments A[q], B[q] of the next step
+    //                       (+ in step 0 and 1: four global loads)
+    //   step 3,    group q: write four chunks of the next stage to LDS
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4_t af[4], bfr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = frag(sa, wm * 128 + i * 32 + p, 2 * s + h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = frag(sb, wn * 128 + j * 32 + p, 2 * s + h);
-      mma_block(acc, af, bfr, tag);
-    }
-    if (more) {
-      stage_store(smem + (cur ^ 1) * kStageBytes, ra);
-      stage_store(smem + (2 + (cur ^ 1)) * kStageBytes, rb);
+      for (int q = 0; q < 4; ++q) {
+        if (s < 3) {
+          fa[(s + 1) & 1][q] = frag(sa, arow + q * 32, 2 * (s + 1) + h);
+          fb[(s + 1) & 1][q] = frag(sb, brow + q * 32, 2 * (s + 1) + h);
+        }
+        if (s < 2) {
+          const int g = s * 4 + q;  // 0..7: two A and two B chunks
+          if (g < 4) {
+            ra[2 * g] = __builtin_amdgcn_raw_buffer_load_b128(rsa, (int)(ga + (2 * g) * 32 * rowa), 0, 0);
+            ra[2 * g + 1] = __builtin_amdgcn_raw_buffer_load_b128(rsa, (int)(ga + (2 * g + 1) * 32 * rowa), 0, 0);
+          } else {
+            const int gg = g - 4;
+            rb[2 * gg] = __builtin_amdgcn_raw_buffer_load_b128(rsb, (int)(gb + (2 * gg) * 32 * rowbb), 0, 0);
+            rb[2 * gg + 1] = __builtin_amdgcn_raw_buffer_load_b128(rsb, (int)(gb + (2 * gg + 1) * 32 * rowbb), 0, 0);
+          }
+        }
+        if (s == 3) {
+          *reinterpret_cast<u32x4_t*>(wa + (2 * q) * 32 * kRowBytes) = ra[2 * q];
+          *reinterpret_cast<u32x4_t*>(wa + (2 * q + 1) * 32 * kRowBytes) = ra[2 * q + 1];
+          *reinterpret_cast<u32x4_t*>(wb + (2 * q) * 32 * kRowBytes) = rb[2 * q];
+          *reinterpret_cast<u32x4_t*>(wb + (2 * q + 1) * 32 * kRowBytes) = rb[2 * q + 1];
+        }
+        mma_row(acc[q], fa[s & 1][q], fb[s & 1], tag);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __syncthreads();
+    const char* na = smem + (cur ^ 1) * kStageBytes;
+    const char* nb = smem + (2 + (cur ^ 1)) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = frag(na, arow + i * 32, h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[0][j] = frag(nb, brow + j * 32, h);
   }
+  __syncthreads();
 }
 
 // Workgroup L is dispatched to XCD (L mod 8). Renumber so that the workgroups

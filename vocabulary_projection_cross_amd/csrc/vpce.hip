@@ -460,20 +460,28 @@ void prod_kernel(ProdParams a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int p = lane & 31, h = lane >> 5;
+  // Loads of the old values are all issued before any store, so they
+  // overlap instead of serialising on possible aliasing.
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int64_t col = n0 + wn * 128 + jj * 32 + p;
-    if (col >= a.Nc) continue;
+    const bool cok = col < a.Nc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      float old[16];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int64_t row = m0 + wm * 128 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        if (row < a.M) {
-          float* o = a.out + row * a.ldo + col;
-          const float v = acc[i][jj][rr];
-          *o = a.accumulate ? *o + v : v;
-        }
+        old[rr] = (a.accumulate && cok && row < a.M)
+                      ? __builtin_nontemporal_load(a.out + row * a.ldo + col)
+                      : 0.f;
+      }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        if (cok && row < a.M)
+          __builtin_nontemporal_store(acc[i][jj][rr] + old[rr],
+                                      a.out + row * a.ldo + col);
       }
     }
   }
