@@ -3,15 +3,30 @@ cross-entropy on one MI355X.
 
 A step is one vpce_forward + one vpce_backward over the whole batch of the
 one-GPU slice of a 1M-token context (N=65536 tokens, d=7168, V=129280, R=8
-shards, bf16 inputs, fp32 accumulation and gradients), inputs resident in HBM.
-Prints ONE JSON line.
+shards, bf16 inputs, fp32 accumulation and gradients), with the inputs already
+resident in HBM. Prints ONE JSON line on stdout.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--copy-calibration]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--cpu-seconds S] [--input-cache DIR]
+    python bench.py --copy-calibration   # plain 1 GiB device copies, for
+                                         # scaling HBM traffic counters
+
+Roofline: the dominant single launch is the forward tile kernel
+(fwd_lse_kernel: 2*N*d*V MFMA flops in one launch). Its duration is measured
+with HIP events recorded on the stream the library launches on (the current
+torch stream, which the binding passes to the C ABI), bracketing each
+vpce_forward call of the timed steps; the bracket also holds three
+microsecond-scale kernels (target fill, partial merge, loss), so the figure
+slightly understates the kernel's own rate. HBM traffic per launch comes from
+rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs of this same script, scaled by
+the counters' reading for plain device copies of known size; it is stored in
+profiles/ with a hash of the kernel sources and reported only while the
+sources still match.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,17 +38,46 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
 PEAK_F32_TFLOPS = 157.3
 HEADLINE = "ctx1m_slice_n64k_d7168_v129k_r8"
+KERNEL_SOURCES = ("vocabulary_projection_cross_amd/csrc/vpce.hip",
+                  "vocabulary_projection_cross_amd/csrc/tile_core.hpp")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so
+    that only a change of code makes stored counter readings stale."""
+    import re
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(workload: str):
+    """Measured HBM bytes per fwd_lse_kernel launch, if the stored counter
+    summary was taken from the current kernel sources."""
+    path = os.path.join(ROOT, "profiles",
+                        f"fwd_lse_kernel_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec
+
+
 def cpu_baseline(inp, target_s=15.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same
     workload: the first n tokens against the full vocabulary (forward and
     backward, 6 n d V flops). Returns tokens/s and the sample description."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
@@ -54,16 +98,19 @@ def cpu_baseline(inp, target_s=15.0):
     n = max(probe_n, (n // 32) * 32)
     t = run(n)
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    blas = ",".join(sorted({d.get("internal_api", "?")
+                            for d in threadpool_info()}))
     del Wf
     return {"value": n / t, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"first {n} of {w.N} tokens, full V={w.V}, d={w.d}; "
-                      f"fp64 numpy forward+backward in {t:.1f} s "
+                      f"fp64 numpy ({blas}) forward+backward in {t:.1f} s "
                       f"({6.0 * n * w.d * w.V / t / 1e9:.1f} GFLOP/s)"}
 
 
 def copy_calibration():
-    """A plain device copy of known size, for scaling HBM traffic counters."""
+    """Plain device copies of known size, for scaling HBM traffic counters:
+    3 copies of 1 GiB (each reads 1 GiB and writes 1 GiB)."""
     import torch
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -72,7 +119,29 @@ def copy_calibration():
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": n, "note": "3 copies of 1 GiB"}))
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+
+
+def load_inputs(w, cache_dir):
+    """Seeded synthetic inputs; optionally kept as .npy files under cache_dir
+    so repeated runs in one session skip the generation."""
+    import numpy as np
+
+    import workloads as WL
+    if cache_dir:
+        os.makedirs(cache_dir, exist_ok=True)
+        stem = os.path.join(cache_dir, f"{w.name}_seed0")
+        names = ("H", "W", "labels", "outliers")
+        if all(os.path.exists(f"{stem}_{k}.npy") for k in names):
+            arr = {k: np.load(f"{stem}_{k}.npy", mmap_mode="r") for k in names}
+            return WL.Inputs(w, arr["H"], arr["W"], np.array(arr["labels"]),
+                             np.array(arr["outliers"]))
+        inp = WL.make_inputs(w, 0)
+        for k, v in (("H", inp.H), ("W", inp.W), ("labels", inp.labels),
+                     ("outliers", inp.outlier_rows)):
+            np.save(f"{stem}_{k}.npy", v)
+        return inp
+    return WL.make_inputs(w, 0)
 
 
 def main():
@@ -83,13 +152,14 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--input-cache", default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
-              "path (the ring over several GPUs is design-only). Run with "
-              "--gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the path across several GPUs "
+              "(the ring of shards over RCCL) is not built, only described. "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
@@ -103,15 +173,17 @@ def main():
 
     w = WL.BY_NAME[args.workload]
     log(f"bench: generating {w.name} inputs")
-    inp = WL.make_inputs(w, 0)
+    inp = load_inputs(w, args.input_cache)
     dev = torch.device("cuda:0")
     if w.dtype == "bf16":
-        H = torch.from_numpy(inp.H.view(np.int16)).to(dev).view(torch.bfloat16)
-        W = torch.from_numpy(inp.W.view(np.int16)).to(dev).view(torch.bfloat16)
+        H = torch.from_numpy(np.ascontiguousarray(inp.H).view(np.int16)).to(
+            dev).view(torch.bfloat16)
+        W = torch.from_numpy(np.ascontiguousarray(inp.W).view(np.int16)).to(
+            dev).view(torch.bfloat16)
     else:
-        H = torch.from_numpy(inp.H).to(dev)
-        W = torch.from_numpy(inp.W).to(dev)
-    lab = torch.from_numpy(inp.labels).to(dev)
+        H = torch.from_numpy(np.ascontiguousarray(inp.H)).to(dev)
+        W = torch.from_numpy(np.ascontiguousarray(inp.W)).to(dev)
+    lab = torch.from_numpy(np.ascontiguousarray(inp.labels)).to(dev)
     dloss = torch.ones(1, dtype=torch.float32, device=dev)
     ws = torch.empty(vp.workspace_bytes(w.N, w.d, w.V, w.R, H.dtype),
                      dtype=torch.uint8, device=dev)
@@ -127,16 +199,18 @@ def main():
     for _ in range(args.warmup):
         out = step()
     torch.cuda.synchronize()
-    del out
+    out = None
 
+    # the binding launches on torch's current stream; record there
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    log(f"bench: timing {args.steps} steps")
-    torch.cuda.synchronize()
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
     t_all0.record(stream)
     for k in range(args.steps):
         ev[k][0].record(stream)
@@ -146,11 +220,12 @@ def main():
         ev[k][2].record(stream)
     t_all1.record(stream)
     torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
     total_ms = t_all0.elapsed_time(t_all1)
     fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
     bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
     out_bytes = sum(t.numel() * t.element_size() for t in (loss, lse, dH, dW))
-    # peak device bytes of one step, previous outputs released
+    # peak device bytes of one step, the previous outputs released
     del loss, lse, dH, dW
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
@@ -161,12 +236,13 @@ def main():
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     peak_tf = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    # dominant single launch: the forward tile kernel (2 N d V flops); its
-    # launch is bracketed by the forward events (the three other forward
-    # kernels take microseconds and are included, which only lowers the
-    # figure)
     fwd_avg = float(np.mean(fwd_ms))
-    fwd_tf = 2.0 * w.N * w.d * w.V / (fwd_avg * 1e-3) / 1e12
+    fwd_flops = 2.0 * w.N * w.d * w.V
+    fwd_tf = fwd_flops / (fwd_avg * 1e-3) / 1e12
+    trec = traffic_record(w.name)
+    traffic = None
+    if trec is not None:
+        traffic = int(trec["hbm_bytes_per_launch"])
     result = {
         "metric": "fwd+bwd tokens/s of blocked vocab-proj CE; % bf16 MFMA "
                   "peak; peak bytes",
@@ -180,15 +256,16 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded; H~N(0,1), W scaled for logit std 3, "
-                "Zipf(1.1) labels, 2% ignored)" if w.name == HEADLINE else
-                "synthetic (seeded)",
+        "data": ("synthetic (seeded; H~N(0,1), W scaled for logit std 3, "
+                 "Zipf(1.1) labels over a permuted vocabulary, 2% ignored)"
+                 if w.name == HEADLINE else "synthetic (seeded)"),
         "config": {"workload": w.name, "N": w.N, "d": w.d, "V": w.V,
                    "R": w.R, "global_batch": w.N, "parallelism": "none"},
         "tflops": tflops,
         "pct_mfma_peak": 100.0 * tflops / peak_tf,
         "fwd_ms": fwd_avg,
         "bwd_ms": float(np.mean(bwd_ms)),
+        "host_wall_ms_per_step": wall_ms,
         "peak_bytes": int(peak),
         "peak_bytes_split": {"inputs": int(in_bytes),
                              "outputs": int(out_bytes),
@@ -197,11 +274,15 @@ def main():
                                           ws.numel())},
         "roofline": {"bound": "mfma", "kernel": "fwd_lse_kernel",
                      "achieved": fwd_tf, "peak": peak_tf, "unit": "TFLOP/s",
-                     "frac": fwd_tf / peak_tf, "traffic": None},
+                     "frac": fwd_tf / peak_tf, "traffic": traffic,
+                     "flops_per_launch": fwd_flops,
+                     "launch_ms": fwd_avg},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on a sample (CPU baseline)")
+        del H, W, lab, dH, dW, ws
+        torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

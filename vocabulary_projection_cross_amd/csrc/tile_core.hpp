@@ -1,20 +1,22 @@
 // tile_core.hpp -- the MFMA tile engine shared by every GEMM phase of the
 // blocked vocabulary-projection cross-entropy on gfx950 (CDNA4).
 //
-// One workgroup of 256 threads (4 wave64s in a 2x2 arrangement) computes a
-// 256 x 256 fp32 tile C = A . B^T where A [M x K] and B [Nc x K] are both
-// row-major with K contiguous ("NT" form). Each wave owns a 128 x 128 sub-tile
-// held as 4 x 4 accumulators of the 32x32 MFMA layout:
+// A workgroup computes one 256 x 256 fp32 tile C = A . B^T where A [M x K]
+// and B [Nc x K] are both row-major with K contiguous ("NT" form). Its waves
+// split the tile as Layout<WM, WN> says (4 x 2 waves of 64 x 128 by default,
+// two waves per SIMD); each wave holds its sub-tile as R x C accumulators of
+// the 32x32 MFMA layout:
 //   element r (0..15) of accumulator (i, j) on lane l is
 //   row = i*32 + 8*(r/4) + 4*(l/32) + (r%4),  col = j*32 + (l%32)
 // within the wave's sub-tile.
 //
-// K is consumed in stages of 128 bytes per row (64 bf16 or 32 fp32): the two
-// operand tiles of a stage are 256 rows x 128 B each, double-buffered in LDS
-// (4 x 32 KiB). Rows are stored with the 16-byte chunk index XOR-swizzled by
-// the row, so that both the coalesced stage writes and the MFMA fragment reads
-// (16 consecutive rows, same chunk) touch distinct banks whether the LDS
-// services 8 or 16 lanes of a 128-bit access per cycle.
+// Operands stream through a ring of NST LDS stages of RB bytes of K per row
+// (64 B x 4 stages by default), copied global -> LDS by buffer loads that
+// write LDS directly, NST - 1 stages ahead of the MFMAs. Within a row the
+// 16-byte chunk index is XOR-swizzled by row bits, so the MFMA fragment reads
+// (consecutive rows, same chunk) hit distinct banks whether the LDS serves 8
+// or 16 lanes of a 128-bit read per cycle; the copies write 1 KiB contiguous
+// blocks.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,246 +28,356 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kTile = 256;          // BM = BN
-constexpr int kRowBytes = 128;      // bytes of K per row per stage
-constexpr int kStageBytes = kTile * kRowBytes;   // 32 KiB
-constexpr int kGemmLds = 4 * kStageBytes;        // A,B x 2 stages = 128 KiB
+constexpr int kTile = 256;                          // BM = BN
+constexpr int kGemmLds = 128 * 1024;                // LDS of the operand ring
 
 // Elements of T per 16-byte chunk.
 template <typename T> struct Chunk;
 template <> struct Chunk<__bf16> { static constexpr int E = 8; };
 template <> struct Chunk<float> { static constexpr int E = 4; };
 
-__device__ __forceinline__ int swz(int row) {
-  return (row & 7) ^ ((row >> 3) & 1);
-}
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
-}
+// How the waves of a workgroup split the 256 x 256 tile: WM x WN waves, each
+// owning a (256/WM) x (256/WN) sub-tile held as R x C accumulators of the
+// 32x32 MFMA layout. Wave w sits at (w / WN, w % WN). With 8 waves two of
+// them share each SIMD, so one wave's MFMAs keep the matrix unit busy while
+// the other waits to issue a copy or an LDS read.
+template <int WM_, int WN_>
+struct Layout {
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWaveRows = kTile / WM;
+  static constexpr int kWaveCols = kTile / WN;
+  static constexpr int R = kWaveRows / 32;  // accumulator row blocks
+  static constexpr int C = kWaveCols / 32;  // accumulator column blocks
+};
 
-// One "chunk pair" step of the wave's 4 x 4 accumulators: each lane supplies
-// 16 bytes of A for each of its 4 row blocks and 16 bytes of B for each of
-// its 4 column blocks.
+// Shape of the operand ring: RB bytes of K per row per stage, NST stages.
+// A stage holds both 256-row operand tiles; copies run NST - 1 stages ahead.
+//   RB = 64:  chunk slot = chunk ^ ((row >> 1) ^ (row >> 2)) & 3
+//   RB = 128: chunk slot = chunk ^ (row & 7) ^ ((row >> 3) & 1)
+// Either way, 8 consecutive rows read at one chunk fill a 128-byte bank
+// window exactly once and 16 consecutive rows fill a 256-byte window once.
+template <int RB, int NST, int WAVES>
+struct Ring {
+  static_assert(RB == 64 || RB == 128, "row bytes per stage");
+  static constexpr int kChunks = RB / 16;              // chunks per row
+  static constexpr int kSteps = RB / 32;               // MFMA K-steps
+  static constexpr int kBlockRows = 1024 / RB;         // rows per 1 KiB copy
+  static constexpr int kBlocks = kTile / kBlockRows / WAVES;  // per wave/op
+  static constexpr int kOperandBytes = kTile * RB;
+  static constexpr int kStageBytes = 2 * kOperandBytes;
+  static constexpr int kCopies = 2 * kBlocks;          // per wave per stage
+  static_assert(kBlocks >= 1, "every wave copies at least one block");
+  static_assert(RB == 64 || kBlocks % 2 == 0, "block parity fixes the swizzle");
+  static_assert(NST * kStageBytes <= kGemmLds, "ring exceeds LDS budget");
+  __device__ static constexpr int swz(int row) {
+    return RB == 64 ? ((row >> 1) ^ (row >> 2)) & 3
+                    : (row & 7) ^ ((row >> 3) & 1);
+  }
+};
+
+// One K-step of one accumulator row block (C accumulators sharing the A
+// fragment): each lane supplies 16 bytes of A and 16 bytes of B per block.
 //   bf16: one v_mfma_f32_32x32x16_bf16 per accumulator (lane half h carries
-//         k = 8h..8h+7 of the chunk pair).
+//         k = 8h..8h+7 of the step's 16).
 //   fp32: four v_mfma_f32_32x32x2_f32 per accumulator; instruction e pairs
 //         element e of the two halves' chunks. Any pairing of k between A and
-//         B that is the same on both operands gives the same sum. The e loop
-//         is outermost so that dependent instructions are 16 apart.
+//         B that is the same on both operands gives the same sum.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void mma_block(f32x16_t (&acc)[4][4],
-                                          const u32x4_t (&a)[4],
-                                          const u32x4_t (&b)[4],
-                                          const __bf16*) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, b[j]),
-          acc[i][j], 0, 0, 0);
-}
-__device__ __forceinline__ void mma_block(f32x16_t (&acc)[4][4],
-                                          const u32x4_t (&a)[4],
-                                          const u32x4_t (&b)[4],
-                                          const float*) {
-  f32x4_t af[4], bf[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    af[i] = __builtin_bit_cast(f32x4_t, a[i]);
-    bf[i] = __builtin_bit_cast(f32x4_t, b[i]);
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][e], bf[j][e],
-                                                         acc[i][j], 0, 0, 0);
-}
-
-// One accumulator row block (4 accumulators sharing the A fragment).
-__device__ __forceinline__ void mma_row(f32x16_t (&acc)[4], u32x4_t a,
-                                        const u32x4_t (&b)[4],
+template <int C>
+__device__ __forceinline__ void mma_row(f32x16_t (&acc)[C], u32x4_t a,
+                                        const u32x4_t (&b)[C],
                                         const __bf16*) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < C; ++j)
     acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[j]),
         acc[j], 0, 0, 0);
 }
-__device__ __forceinline__ void mma_row(f32x16_t (&acc)[4], u32x4_t a,
-                                        const u32x4_t (&b)[4], const float*) {
+template <int C>
+__device__ __forceinline__ void mma_row(f32x16_t (&acc)[C], u32x4_t a,
+                                        const u32x4_t (&b)[C], const float*) {
   const f32x4_t af = __builtin_bit_cast(f32x4_t, a);
-  f32x4_t bf[4];
+  f32x4_t bf[C];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bf[j] = __builtin_bit_cast(f32x4_t, b[j]);
+  for (int j = 0; j < C; ++j) bf[j] = __builtin_bit_cast(f32x4_t, b[j]);
 #pragma unroll
   for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < C; ++j)
       acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[j][e], acc[j],
                                                     0, 0, 0);
 }
 
-// A buffer resource over the valid rows of one operand tile: loads past its
-// end return zero, which masks ragged row tails without branches.
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource (as four dwords) over the valid rows of one operand
+// tile: loads past its end return zero, which masks ragged row tails.
 template <typename T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* base,
-                                                            int64_t ld,
-                                                            int rows) {
+__device__ __forceinline__ i32x4_t tile_rsrc_dw(const T* base, int64_t ld,
+                                                int rows) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
   const uint32_t bytes = (uint32_t)((int64_t)rows * ld * (int64_t)sizeof(T));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0,
-                                           (int)bytes, 0x00020000);
+  return i32x4_t{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), (int)bytes,
+                 0x00020000};
 }
 
-// Global -> registers for one 256-row x 128-byte stage of an operand.
-// Thread t loads chunks q = u*256 + t (u = 0..7): row q/8, chunk q%8, so each
-// group of 8 threads reads one row's 128 contiguous bytes. Rows past the
-// resource and chunks at or beyond K read as zero.
-template <typename T>
-__device__ __forceinline__ void stage_load(u32x4_t (&r)[8],
-                                           __amdgpu_buffer_rsrc_t rs,
-                                           int64_t ld, int64_t k0,
-                                           int64_t K) {
-  constexpr int E = Chunk<T>::E;
-  const int t = threadIdx.x;
-  const int row0 = t >> 3, c = t & 7;
-  const int64_t k = k0 + c * E;
-  const uint32_t rowb = (uint32_t)(ld * (int64_t)sizeof(T));
-  const uint32_t off = k < K ? (uint32_t)row0 * rowb + (uint32_t)(k * (int64_t)sizeof(T))
-                             : 0x80000000u;
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    r[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + u * 32 * rowb), 0, 0);
+// 16 bytes per lane from global memory (resource rs, byte offset voff) into
+// LDS at lds_addr + 16 * lane. Written as one asm statement so that the
+// compiler's wait insertion does not track it as an LDS store: it would
+// otherwise wait for every outstanding copy before unrelated LDS reads. The
+// caller orders copies and reads with explicit s_waitcnt and s_barrier.
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds_addr,
+                                              uint32_t voff, i32x4_t rs) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rs)
+      : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
-__device__ __forceinline__ void stage_store(char* stage,
-                                            const u32x4_t (&r)[8]) {
-  const int t = threadIdx.x;
-  const int row0 = t >> 3, c = t & 7;
-  char* p = stage + lds_off(row0, c);
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    *reinterpret_cast<u32x4_t*>(p + u * 32 * kRowBytes) = r[u];
+// A byte offset that every buffer resource here rejects (loads read zero).
+// Resources span less than 2^31 bytes and a block offset (fewer than 32
+// blocks of at most 16 rows, rows below 2^23 bytes) added to it stays below
+// 2^32, so it stays rejected.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt_hi[15:14]); unnamed counters left at their maximum.
+constexpr int waitcnt_vm_lgkm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
 }
 
-__device__ __forceinline__ u32x4_t frag(const char* stage, int row,
-                                        int chunk) {
-  return *reinterpret_cast<const u32x4_t*>(stage + lds_off(row, chunk));
-}
-
-// acc = A[0:256, 0:K] . B[0:256, 0:K]^T for the workgroup's tile.
-// A, B point at the tile's first row; a_rows / b_rows are the valid rows
-// (clamped by the caller to [0, 256]); 256 * ld * sizeof(T) must stay below
-// 2^31 bytes (checked on the host). smem must hold kGemmLds bytes.
-// Ends with a workgroup barrier, so smem may be rewritten right after.
-template <typename T>
-__device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[4][4],
-                                              const T* __restrict__ A,
-                                              int64_t lda, int a_rows,
-                                              const T* __restrict__ B,
-                                              int64_t ldb, int b_rows,
-                                              int64_t K, char* smem) {
-  constexpr int BK = 8 * Chunk<T>::E;  // elements of K per stage
+// acc = A[0:256, 0:K] . B[0:256, 0:K]^T for the workgroup's tile; this wave's
+// sub-tile lands in acc (layout L). A, B point at the tile's first row;
+// a_rows / b_rows are the valid rows (clamped by the caller to [0, 256]);
+// 256 * ld * sizeof(T) must stay below 2^31 bytes and K must be a multiple of
+// 16 bytes' worth of T (checked on the host). smem must hold kGemmLds bytes.
+// Ends with every copy landed and a workgroup barrier, so smem may be reused
+// right after.
+//
+// Global memory is copied straight into LDS by the buffer-load-to-LDS path
+// (no register staging): each wave copies kBlocks 1 KiB blocks of each
+// operand per stage; lane l of a block copies row l / kChunks into slot
+// l % kChunks of that row, which holds the global chunk slot ^ swz(row).
+// Per stage kt (ring buffer kt % NST), each of its S K-steps runs R row
+// groups of C MFMAs; alongside them the wave
+//   reads the next step's fragments (A0 and the B fragments first, which the
+//   next step's first row group needs),
+//   issues the copies of stage kt + NST - 1 into buffer (kt - 1) % NST, spread
+//   over the row groups (every wave passed the previous stage's barrier
+//   after its reads of that buffer completed);
+// and in the last step, after the first row group, waits for its copies of
+// stage kt + 1 (later stages' copies may stay outstanding) and its own LDS
+// reads, joins the workgroup barrier, then reads stage kt + 1's first
+// fragments.
+template <typename T, typename L, int RB, int NST>
+__device__ __forceinline__ void tile_mainloop_ring(
+    f32x16_t (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
+    int a_rows, const T* __restrict__ B, int64_t ldb, int b_rows, int64_t K,
+    char* smem) {
+  using P = Ring<RB, NST, L::kWaves>;
+  constexpr int R = L::R, C = L::C;
+  constexpr int E = Chunk<T>::E;           // elements per 16-byte chunk
+  constexpr int BK = RB / (int)sizeof(T);  // elements of K per stage
+  constexpr int S = P::kSteps;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int swave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
+  const int wm = wave / L::WN, wn = wave % L::WN;
   const int p = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < R; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < C; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = (int)((K + BK - 1) / BK);
   if (KT <= 0) return;
-  u32x4_t ra[8], rb[8];
-  const __amdgpu_buffer_rsrc_t rsa = tile_rsrc<T>(A, lda, a_rows);
-  const __amdgpu_buffer_rsrc_t rsb = tile_rsrc<T>(B, ldb, b_rows);
-  stage_load<T>(ra, rsa, lda, 0, K);
-  stage_load<T>(rb, rsb, ldb, 0, K);
-  stage_store(smem, ra);
-  stage_store(smem + 2 * kStageBytes, rb);
-  __syncthreads();
+  const i32x4_t rsa = tile_rsrc_dw<T>(A, lda, a_rows);
+  const i32x4_t rsb = tile_rsrc_dw<T>(B, ldb, b_rows);
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_char_t*)smem;
+
+  // copy side: blocks kBlocks*w .. kBlocks*w + kBlocks-1 of both operands.
+  // The swizzle of a row depends on its bits 0..3; block starts are
+  // multiples of kBlockRows, so the lane's chunk depends on the block only
+  // through bit 3 of its first row (RB = 128: blocks of 8 rows, an even
+  // number per wave, so that bit is the parity of u).
+  const int crow = lane / P::kChunks;
+  const int slot = lane % P::kChunks;
+  const int ch0 = slot ^ P::swz(crow);
+  const int ch1 = slot ^ P::swz(crow + 8);
+  const uint32_t pa = (uint32_t)(lda * (int64_t)sizeof(T));
+  const uint32_t pb = (uint32_t)(ldb * (int64_t)sizeof(T));
+  const uint32_t row0 = (uint32_t)(swave * P::kBlocks * P::kBlockRows + crow);
+  const uint32_t cdst = lds + (uint32_t)(swave * P::kBlocks * 1024);
+  // stages whose chunk (for even/odd blocks) lies inside K:
+  // s * BK + ch * E < K  <=>  s < klim
+  const int Ki = (int)K;  // K < 2^31 (checked on the host)
+  const int klim0 = Ki > ch0 * E ? (Ki - ch0 * E + BK - 1) / BK : 0;
+  const int klim1 = Ki > ch1 * E ? (Ki - ch1 * E + BK - 1) / BK : 0;
+  const uint32_t ra0 = row0 * pa + (uint32_t)(ch0 * 16);
+  const uint32_t ra1 = row0 * pa + (uint32_t)(ch1 * 16);
+  const uint32_t rb0 = row0 * pb + (uint32_t)(ch0 * 16);
+  const uint32_t rb1 = row0 * pb + (uint32_t)(ch1 * 16);
+  uint32_t va[2], vb[2];
+  // lane offsets of stage s for even/odd blocks (past K -> out of range)
+  auto stage_offsets = [&](int s) {
+    const uint32_t ko = (uint32_t)s * (uint32_t)RB;
+    va[0] = s < klim0 ? ra0 + ko : kOutOfRange;
+    vb[0] = s < klim0 ? rb0 + ko : kOutOfRange;
+    if (RB == 128) {
+      va[1] = s < klim1 ? ra1 + ko : kOutOfRange;
+      vb[1] = s < klim1 ? rb1 + ko : kOutOfRange;
+    }
+  };
+  // copy c of a stage: even c -> A block c/2, odd c -> B block c/2
+  auto copy_one = [&](int s, int c) {
+    const int u = c >> 1;
+    const uint32_t dst =
+        cdst + (uint32_t)((s % NST) * P::kStageBytes + u * 1024);
+    const int e = (RB == 128) ? (u & 1) : 0;
+    const uint32_t rows = (uint32_t)(u * P::kBlockRows);
+    if ((c & 1) == 0)
+      copy16_to_lds(dst, va[e] + rows * pa, rsa);
+    else
+      copy16_to_lds(dst + P::kOperandBytes, vb[e] + rows * pb, rsb);
+  };
+
+  // fragment side: lane (p, h) reads row (base + 32*i + p) at chunk 2s + h;
+  // rows differ from p by multiples of 32, so the swizzle is swz(p).
+  const int g = P::swz(p);
+  const int fa = (wm * L::kWaveRows + p) * RB;
+  const int fb = P::kOperandBytes + (wn * L::kWaveCols + p) * RB;
+  int fo[S];
+#pragma unroll
+  for (int st = 0; st < S; ++st) fo[st] = ((2 * st + h) ^ g) << 4;
+  u32x4_t af[2][R], bfr[2][C];
+  // read number n of a step's R + C fragment reads: A0, B0..B(C-1),
+  // A1..A(R-1)
+  constexpr int kReads = R + C;
+  auto read_one = [&](int stage_off, int st, int buf, int n) {
+    if (n == 0 || n > C) {
+      const int i = n == 0 ? 0 : n - C;
+      af[buf][i] = *reinterpret_cast<const u32x4_t*>(
+          smem + stage_off + fa + fo[st] + i * 32 * RB);
+    } else {
+      const int j = n - 1;
+      bfr[buf][j] = *reinterpret_cast<const u32x4_t*>(
+          smem + stage_off + fb + fo[st] + j * 32 * RB);
+    }
+  };
+  // reads [n0, n1) of a step
+  auto reads = [&](int stage_off, int st, int buf, int n0, int n1) {
+#pragma unroll
+    for (int n = 0; n < kReads; ++n)
+      if (n >= n0 && n < n1) read_one(stage_off, st, buf, n);
+  };
+
+  for (int st = 0; st < NST - 1; ++st) {
+    stage_offsets(st);
+#pragma unroll
+    for (int c = 0; c < P::kCopies; ++c) copy_one(st, c);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm((NST - 2) * P::kCopies, 15));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  reads(0, 0, 0, 0, kReads);
   const T* tag = nullptr;
-  // Software pipeline, per stage of 4 chunk-pair steps:
-  //   step 0: issue the next stage's global loads; read step 1's fragments
-  //   steps 1, 2: read the following step's fragments
-  //   step 3: write the next stage into the other LDS buffer
-  // each while the MFMAs of the current step run; then one barrier and the
-  // next stage's step-0 fragments. Past the last stage the loads fall
-  // outside the resource (zeros) and land in the idle buffer.
-  u32x4_t fa[2][4], fb[2][4];
-  const int arow = wm * 128 + p, brow = wn * 128 + p;
+
+  // Copies are spread evenly over the stage's S * R row groups. With a
+  // 2-deep ring the copies of stage kt + 1 must all be issued before the
+  // barrier of stage kt (which waits for them), so they go into the row
+  // groups up to the last step's first one.
+  constexpr int kGroups = S * R;
+  constexpr int kBarrierGroup = (S - 1) * R;  // group after which we wait
+  constexpr int kSpread = NST >= 3 ? kGroups : kBarrierGroup + 1;
+  auto copies_at = [&](int s, int grp) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa[0][i] = frag(smem, arow + i * 32, h);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) fb[0][j] = frag(smem + 2 * kStageBytes, brow + j * 32, h);
-  constexpr int E = Chunk<T>::E;
-  const int t = threadIdx.x;
-  const uint32_t rowa = (uint32_t)(lda * (int64_t)sizeof(T));
-  const uint32_t rowbb = (uint32_t)(ldb * (int64_t)sizeof(T));
-  const uint32_t base_a = (uint32_t)(t >> 3) * rowa + (uint32_t)((t & 7) * E * sizeof(T));
-  const uint32_t base_b = (uint32_t)(t >> 3) * rowbb + (uint32_t)((t & 7) * E * sizeof(T));
-  const int st_off = lds_off(t >> 3, t & 7);
+    for (int c = 0; c < P::kCopies; ++c)
+      if (c * kSpread / P::kCopies == grp) copy_one(s, c);
+  };
+  // copies of the newest stage issued by the barrier point; the copies that
+  // may still be outstanding there are those of the stages after kt + 1
+  constexpr int kIssuedByBarrier =
+      (kBarrierGroup + 1) * P::kCopies / kSpread +
+      ((kBarrierGroup + 1) * P::kCopies % kSpread ? 1 : 0);
+  constexpr int kVmAllowed =
+      NST >= 3 ? (NST - 3) * P::kCopies +
+                     (kIssuedByBarrier < P::kCopies ? kIssuedByBarrier
+                                                    : P::kCopies)
+               : 0;
+  static_assert(kVmAllowed <= 63, "vmcnt range");
+
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const char* sa = smem + cur * kStageBytes;
-    const char* sb = smem + (2 + cur) * kStageBytes;
-    char* wa = smem + (cur ^ 1) * kStageBytes + st_off;
-    char* wb = smem + (2 + (cur ^ 1)) * kStageBytes + st_off;
-    // next stage's global offsets (past K: outside the resource -> zeros)
-    const int64_t kn = (int64_t)(kt + 1) * BK + (t & 7) * E;
-    const bool kin = kn < K;
-    const uint32_t ga = kin ? base_a + (uint32_t)((kt + 1) * BK * sizeof(T)) : 0x80000000u;
-    const uint32_t gb = kin ? base_b + (uint32_t)((kt + 1) * BK * sizeof(T)) : 0x80000000u;
-    // The stage is issued as 16 groups of 4 MFMAs; sched_barrier keeps
-    // each group's memory operations next to its MFMAs:
-    //   steps 0-2, group q: read fragments A[q], B[q] of the next step
-    //                       (+ in step 0 and 1: four global loads)
-    //   step 3,    group q: write four chunks of the next stage to LDS
+    const int cur = (kt % NST) * P::kStageBytes;
+    const int nxt = ((kt + 1) % NST) * P::kStageBytes;
+    stage_offsets(kt + NST - 1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int st = 0; st < S - 1; ++st) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (s < 3) {
-          fa[(s + 1) & 1][q] = frag(sa, arow + q * 32, 2 * (s + 1) + h);
-          fb[(s + 1) & 1][q] = frag(sb, brow + q * 32, 2 * (s + 1) + h);
-        }
-        if (s < 2) {
-          const int g = s * 4 + q;  // 0..7: two A and two B chunks
-          if (g < 4) {
-            ra[2 * g] = __builtin_amdgcn_raw_buffer_load_b128(rsa, (int)(ga + (2 * g) * 32 * rowa), 0, 0);
-            ra[2 * g + 1] = __builtin_amdgcn_raw_buffer_load_b128(rsa, (int)(ga + (2 * g + 1) * 32 * rowa), 0, 0);
-          } else {
-            const int gg = g - 4;
-            rb[2 * gg] = __builtin_amdgcn_raw_buffer_load_b128(rsb, (int)(gb + (2 * gg) * 32 * rowbb), 0, 0);
-            rb[2 * gg + 1] = __builtin_amdgcn_raw_buffer_load_b128(rsb, (int)(gb + (2 * gg + 1) * 32 * rowbb), 0, 0);
-          }
-        }
-        if (s == 3) {
-          *reinterpret_cast<u32x4_t*>(wa + (2 * q) * 32 * kRowBytes) = ra[2 * q];
-          *reinterpret_cast<u32x4_t*>(wa + (2 * q + 1) * 32 * kRowBytes) = ra[2 * q + 1];
-          *reinterpret_cast<u32x4_t*>(wb + (2 * q) * 32 * kRowBytes) = rb[2 * q];
-          *reinterpret_cast<u32x4_t*>(wb + (2 * q + 1) * 32 * kRowBytes) = rb[2 * q + 1];
-        }
-        mma_row(acc[q], fa[s & 1][q], fb[s & 1], tag);
+      for (int q = 0; q < R; ++q) {
+        copies_at(kt + NST - 1, st * R + q);
+        reads(cur, st + 1, (st + 1) & 1, q * kReads / R,
+              (q + 1) * kReads / R);
+        mma_row<C>(acc[q], af[st & 1][q], bfr[st & 1], tag);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();
-    const char* na = smem + (cur ^ 1) * kStageBytes;
-    const char* nb = smem + (2 + (cur ^ 1)) * kStageBytes;
+    constexpr int LB = (S - 1) & 1;
+    copies_at(kt + NST - 1, kBarrierGroup);
+    mma_row<C>(acc[0], af[LB][0], bfr[LB], tag);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kVmAllowed, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (R == 1) reads(nxt, 0, 0, 0, kReads);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = frag(na, arow + i * 32, h);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[0][j] = frag(nb, brow + j * 32, h);
+    for (int q = 1; q < R; ++q) {
+      copies_at(kt + NST - 1, kBarrierGroup + q);
+      reads(nxt, 0, 0, (q - 1) * kReads / (R - 1), q * kReads / (R - 1));
+      mma_row<C>(acc[q], af[LB][q], bfr[LB], tag);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  __syncthreads();
+  // drain the copies issued past K before smem is reused
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, 0));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Build-time shape of the engine (measured on the 1M-context slice: 4 x 2
+// waves with a 4-deep ring of 64-byte slabs is the fastest of the shapes
+// tried; 2 x 2 waves and a 2-deep ring of 128-byte slabs also work).
+#ifndef VPCE_WAVES_M
+#define VPCE_WAVES_M 4
+#endif
+#ifndef VPCE_RING_RB
+#define VPCE_RING_RB 64
+#endif
+#ifndef VPCE_RING_NST
+#define VPCE_RING_NST 4
+#endif
+
+// The configuration every GEMM phase uses.
+using TileLayout = Layout<VPCE_WAVES_M, 2>;
+constexpr int kThreads = TileLayout::kThreads;
+
+template <typename T>
+__device__ __forceinline__ void tile_mainloop(
+    f32x16_t (&acc)[TileLayout::R][TileLayout::C], const T* __restrict__ A,
+    int64_t lda, int a_rows, const T* __restrict__ B, int64_t ldb,
+    int b_rows, int64_t K, char* smem) {
+  tile_mainloop_ring<T, TileLayout, VPCE_RING_RB, VPCE_RING_NST>(
+      acc, A, lda, a_rows, B, ldb, b_rows, K, smem);
 }
 
 // Workgroup L is dispatched to XCD (L mod 8). Renumber so that the workgroups

@@ -36,9 +36,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kChunkCols = 4096;  // backward chunk width C
 constexpr int kMaxSplits = 16;
 constexpr int64_t kMaxTokens = 2000000;
-constexpr int kGroupM = 4;
+// Grouped raster (consecutive workgroups of an XCD share operand rows): how
+// many token / output-row tiles sweep the column tiles together. Measured on
+// the 1M-context slice: 2 suits the forward, 8 the backward products.
+constexpr int kGroupFwd = 2;
+constexpr int kGroupBwd = 8;
 constexpr int kLabIgnored = -2;   // label slot codes in LDS
 constexpr int kLabInvalid = -1;
+using TL = TileLayout;
+constexpr int kWavesPerSimd = TL::kWaves / 4;
+static_assert(TL::WN == 2, "forward row merge pairs two waves per row");
 
 struct Shards {
   int64_t V;
@@ -79,16 +86,16 @@ struct FwdParams {
 };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 void fwd_lse_kernel(FwdParams a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLds];
   __shared__ __attribute__((aligned(16))) int lab_s[kTile];
-  __shared__ float xm[2][256], xs[2][256];
+  __shared__ float xm[TL::WM][TL::R * 64], xs[TL::WM][TL::R * 64];
 
   const int total = a.T * a.R * a.S;
   const int idx = xcd_remap(blockIdx.x, total);
   int it, g;
-  grouped_tile(idx, a.T, a.R * a.S, kGroupM, it, g);
+  grouped_tile(idx, a.T, a.R * a.S, kGroupFwd, it, g);
   const int r = g / a.S, j = g % a.S;
   const Shards sh{a.V, a.R};
   const int64_t v0 = sh.begin(r), vw = sh.width(r);
@@ -98,66 +105,73 @@ void fwd_lse_kernel(FwdParams a) {
 
   const int tid = threadIdx.x;
   const int64_t tok0 = (int64_t)it * kTile;
-  {
+  if (tid < kTile) {
     const int64_t tok = tok0 + tid;
     lab_s[tid] = tok < a.N ? label_code(a.labels[tok], a.ignore_index, a.V)
                            : kLabIgnored;
   }
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int p = lane & 31, h = lane >> 5;
 
   const T* Hb = reinterpret_cast<const T*>(a.H) + tok0 * a.d;
   const int a_rows = clamp_rows(a.N - tok0);
 
   // running (max, sum) in base-2 units for row slot p>>1 of each 32-row block
-  float run_m[4], run_s[4];
+  float run_m[TL::R], run_s[TL::R];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { run_m[i] = -INFINITY; run_s[i] = 0.f; }
-  f32x16_t acc[4][4];
+  for (int i = 0; i < TL::R; ++i) { run_m[i] = -INFINITY; run_s[i] = 0.f; }
+  f32x16_t acc[TL::R][TL::C];
 
   for (int q = q0; q < q1; ++q) {
     const int64_t col0 = v0 + (int64_t)q * kTile;
     const T* Wb = reinterpret_cast<const T*>(a.W) + col0 * a.d;
     tile_mainloop<T>(acc, Hb, a.d, a_rows, Wb, a.d, clamp_rows(vend - col0),
                      a.d, smem);
-    // columns of this lane: lc + 32*jj, jj = 0..3 (global vocabulary index)
-    const int64_t lc = col0 + wn * 128 + p;
-    bool cv[4];
+    // columns of this lane: lc + 32*jj, jj = 0..3 (global vocabulary index;
+    // V < 2^31)
+    const int lc = (int)col0 + wn * TL::kWaveCols + p;
+    const int vend32 = (int)vend;
+    bool cv[TL::C];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) cv[jj] = lc + jj * 32 < vend;
+    for (int jj = 0; jj < TL::C; ++jj) cv[jj] = lc + jj * 32 < vend32;
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TL::R; ++i) {
       float ml[16], sl[16];
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         // 4 consecutive rows: 8*rq + 4*h + (0..3) within the 32-row block
-        const int rowb = wm * 128 + i * 32 + 8 * rq + 4 * h;
+        const int rowb = wm * TL::kWaveRows + i * 32 + 8 * rq + 4 * h;
         const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = rq * 4 + e;
-          float y[4];
+          float y[TL::C];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
+          for (int jj = 0; jj < TL::C; ++jj)
             y[jj] = cv[jj] ? acc[i][jj][rr] * kLog2e : -INFINITY;
-          const float m = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+          float m = y[0];
+#pragma unroll
+          for (int jj = 1; jj < TL::C; ++jj) m = fmaxf(m, y[jj]);
           float s = 0.f;
           if (cv[0]) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) s += fast_exp2(y[jj] - m);
+            for (int jj = 0; jj < TL::C; ++jj) s += fast_exp2(y[jj] - m);
           }
           ml[rr] = m;
           sl[rr] = s;
           // target logit: the label's column is lc + 32*jj for some jj
+          // (label codes of ignored or invalid tokens are negative)
           const int lab = e == 0 ? labs.x : e == 1 ? labs.y : e == 2 ? labs.z : labs.w;
-          const int64_t off = (int64_t)lab - lc;
-          if (lab >= 0 && off >= 0 && off < 128 && (off & 31) == 0 &&
-              (int64_t)lab < vend) {
-            const int jj = (int)(off >> 5);
-            const float z = jj == 0 ? acc[i][0][rr] : jj == 1 ? acc[i][1][rr]
-                          : jj == 2 ? acc[i][2][rr] : acc[i][3][rr];
+          const int off = lab - lc;
+          if (lab >= 0 && (unsigned)off < (unsigned)TL::kWaveCols &&
+              (off & 31) == 0 && lab < vend32) {
+            const int jsel = off >> 5;
+            float z = acc[i][0][rr];
+#pragma unroll
+            for (int jj = 1; jj < TL::C; ++jj)
+              if (jsel == jj) z = acc[i][jj][rr];
             a.tgt[tok0 + rowb + e] = z;
           }
         }
@@ -189,13 +203,14 @@ void fwd_lse_kernel(FwdParams a) {
         ms_merge(ml[0], sl[0], mo, so);
       }
       ms_merge(run_m[i], run_s[i], ml[0], sl[0]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // the two waves sharing rows (wn = 0, 1) combine through LDS
   if (wn == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TL::R; ++i) {
       xm[wm][i * 64 + lane] = run_m[i];
       xs[wm][i * 64 + lane] = run_s[i];
     }
@@ -204,10 +219,10 @@ void fwd_lse_kernel(FwdParams a) {
   if (wn == 0 && (p & 1) == 0) {
     const int rr = p >> 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TL::R; ++i) {
       float m = run_m[i], s = run_s[i];
       ms_merge(m, s, xm[wm][i * 64 + lane], xs[wm][i * 64 + lane]);
-      const int row = wm * 128 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+      const int row = wm * TL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
       const int64_t tok = tok0 + row;
       if (tok < a.N) {
         const int64_t o = (int64_t)(r * a.S + j) * a.N + tok;
@@ -361,7 +376,7 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c,
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 void recompute_g_kernel(GParams a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLds];
   __shared__ __attribute__((aligned(16))) int lab_s[kTile];
@@ -370,38 +385,38 @@ void recompute_g_kernel(GParams a) {
   const int total = a.T * a.CT;
   const int idx = xcd_remap(blockIdx.x, total);
   int it, ct;
-  grouped_tile(idx, a.T, a.CT, kGroupM, it, ct);
+  grouped_tile(idx, a.T, a.CT, kGroupBwd, it, ct);
   const int tid = threadIdx.x;
   const int64_t tok0 = (int64_t)it * kTile;
   const int64_t c0 = (int64_t)ct * kTile;
-  {
+  if (tid < kTile) {
     const int64_t tok = tok0 + tid;
     lab_s[tid] = tok < a.N ? label_code(a.labels[tok], a.ignore_index, a.V)
                            : kLabIgnored;
     lse_s[tid] = tok < a.N ? a.lse[tok] * kLog2e : 0.f;
   }
-  f32x16_t acc[4][4];
+  f32x16_t acc[TL::R][TL::C];
   tile_mainloop<T>(acc, reinterpret_cast<const T*>(a.H) + tok0 * a.d, a.d,
                    clamp_rows(a.N - tok0),
                    reinterpret_cast<const T*>(a.Wc) + c0 * a.d, a.d,
                    clamp_rows(a.C_eff - c0), a.d, smem);
   const float scale = a.scale[0];
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int p = lane & 31, h = lane >> 5;
   T* G = reinterpret_cast<T*>(a.G);
   T* GT = reinterpret_cast<T*>(a.GT);
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int64_t c = c0 + wn * 128 + jj * 32 + p;  // chunk column
+  for (int jj = 0; jj < TL::C; ++jj) {
+    const int64_t c = c0 + wn * TL::kWaveCols + jj * 32 + p;  // chunk column
     const bool cvalid = c < a.C_eff;
     const bool cstore = c < a.C_pad;
     const int v = (int)(a.cv0 + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TL::R; ++i) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int rowb = wm * 128 + i * 32 + 8 * rq + 4 * h;
+        const int rowb = wm * TL::kWaveRows + i * 32 + 8 * rq + 4 * h;
         const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
         const float4 l2 = *reinterpret_cast<const float4*>(&lse_s[rowb]);
         float gv[4];
@@ -443,42 +458,42 @@ struct ProdParams {
 };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 void prod_kernel(ProdParams a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLds];
   const int total = a.TM * a.TN;
   const int idx = xcd_remap(blockIdx.x, total);
   int tm, tn;
-  grouped_tile(idx, a.TM, a.TN, kGroupM, tm, tn);
+  grouped_tile(idx, a.TM, a.TN, kGroupBwd, tm, tn);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
-  f32x16_t acc[4][4];
+  f32x16_t acc[TL::R][TL::C];
   tile_mainloop<T>(acc, reinterpret_cast<const T*>(a.A) + m0 * a.lda, a.lda,
                    clamp_rows(a.M - m0),
                    reinterpret_cast<const T*>(a.B) + n0 * a.ldb, a.ldb,
                    clamp_rows(a.Nc - n0), a.K, smem);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int p = lane & 31, h = lane >> 5;
   // Loads of the old values are all issued before any store, so they
   // overlap instead of serialising on possible aliasing.
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int64_t col = n0 + wn * 128 + jj * 32 + p;
+  for (int jj = 0; jj < TL::C; ++jj) {
+    const int64_t col = n0 + wn * TL::kWaveCols + jj * 32 + p;
     const bool cok = col < a.Nc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TL::R; ++i) {
       float old[16];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        const int64_t row = m0 + wm * TL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
         old[rr] = (a.accumulate && cok && row < a.M)
                       ? __builtin_nontemporal_load(a.out + row * a.ldo + col)
                       : 0.f;
       }
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        const int64_t row = m0 + wm * TL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
         if (cok && row < a.M)
           __builtin_nontemporal_store(acc[i][jj][rr] + old[rr],
                                       a.out + row * a.ldo + col);
