@@ -38,38 +38,49 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
 PEAK_F32_TFLOPS = 157.3
 HEADLINE = "ctx1m_slice_n64k_d7168_v129k_r8"
-KERNEL_SOURCES = ("vocabulary_projection_cross_amd/csrc/vpce.hip",
-                  "vocabulary_projection_cross_amd/csrc/tile_core.hpp")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources with comments and whitespace removed, so
-    that only a change of code makes stored counter readings stale."""
-    import re
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel)) as f:
-            text = f.read()
-        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", " ", text)
-        h.update(" ".join(text.split()).encode())
-    return h.hexdigest()[:16]
+def kernel_code_hash() -> str:
+    """Hash of the device code built into libvpce.so (its .hip_fatbin ELF
+    section), so that stored counter readings go stale exactly when the
+    compiled kernels change, and not when only comments or dead code do."""
+    import struct
+    path = os.path.join(ROOT, "vocabulary_projection_cross_amd", "libvpce.so")
+    with open(path, "rb") as f:
+        elf = f.read()
+    if elf[:4] != b"\x7fELF" or elf[4] != 2:
+        raise RuntimeError(f"{path} is not a 64-bit ELF file")
+    shoff, = struct.unpack_from("<Q", elf, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
+
+    def section(i):
+        name, _, _, _, off, size = struct.unpack_from("<IIQQQQ", elf,
+                                                     shoff + i * shentsize)
+        return name, off, size
+
+    _, stroff, _ = section(shstrndx)
+    for i in range(shnum):
+        name, off, size = section(i)
+        end = elf.index(b"\0", stroff + name)
+        if elf[stroff + name:end] == b".hip_fatbin":
+            return hashlib.sha256(elf[off:off + size]).hexdigest()[:16]
+    raise RuntimeError(f"{path} holds no .hip_fatbin section")
 
 
 def traffic_record(workload: str):
     """Measured HBM bytes per fwd_lse_kernel launch, if the stored counter
-    summary was taken from the current kernel sources."""
+    summary was taken from the device code built now."""
     path = os.path.join(ROOT, "profiles",
                         f"fwd_lse_kernel_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_code_hash") != kernel_code_hash():
         return None
     return rec
 
@@ -92,11 +103,15 @@ def cpu_baseline(inp, target_s=15.0):
         oracle.backward(Hs, Wf, ys)
         return time.perf_counter() - t0
 
-    probe_n = 32
-    t_probe = run(probe_n)
-    n = int(max(probe_n, min(w.N, probe_n * target_s / max(t_probe, 1e-3))))
-    n = max(probe_n, (n // 32) * 32)
+    # Grow the sample until it takes at least half the target: small
+    # samples carry fixed costs (the W conversion, thread start-up) that
+    # make a one-shot extrapolation from a tiny probe undershoot.
+    n = 32
     t = run(n)
+    while t < 0.5 * target_s and n < w.N:
+        grow = min(8.0, target_s / max(t, 1e-3))
+        n = min(w.N, max(n + 32, int(n * grow) // 32 * 32))
+        t = run(n)
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     blas = ",".join(sorted({d.get("internal_api", "?")
                             for d in threadpool_info()}))

@@ -84,3 +84,11 @@ def test_argument_errors_before_launch(lib):
     st = lib.vpce_backward(A, A, A, A, None, 4, 16, 10, 2, -100, 0, A, A, A,
                            16, None)
     assert st == 5
+
+
+def test_device_code_hash_reads_the_built_library():
+    """bench.py keys stored counter readings on the library's device code."""
+    import bench
+    h = bench.kernel_code_hash()
+    assert len(h) == 16 and int(h, 16) >= 0
+    assert bench.kernel_code_hash() == h

@@ -62,7 +62,9 @@ RAGGED = [
     (300, 136, 1000, 3, "f32"),
     (1, 8, 5, 5, "bf16"),
     (64, 64, 33, 33, "f32"),
-    (700, 520, 4500, 1, "bf16"),   # backward chunks of 4096 + ragged tail
+    (700, 520, 4500, 1, "bf16"),
+    (300, 64, 40000, 1, "bf16"),   # one shard over three backward chunks
+                                   # (16384 + 16384 + ragged 7232 columns)
 ]
 
 

@@ -169,16 +169,11 @@ constexpr int waitcnt_vm_lgkm(int vm, int lgkm) {
 // operand per stage; lane l of a block copies row l / kChunks into slot
 // l % kChunks of that row, which holds the global chunk slot ^ swz(row).
 // Per stage kt (ring buffer kt % NST), each of its S K-steps runs R row
-// groups of C MFMAs; alongside them the wave
-//   reads the next step's fragments (A0 and the B fragments first, which the
-//   next step's first row group needs),
-//   issues the copies of stage kt + NST - 1 into buffer (kt - 1) % NST, spread
-//   over the row groups (every wave passed the previous stage's barrier
-//   after its reads of that buffer completed);
-// and in the last step, after the first row group, waits for its copies of
-// stage kt + 1 (later stages' copies may stay outstanding) and its own LDS
-// reads, joins the workgroup barrier, then reads stage kt + 1's first
-// fragments.
+// groups of C MFMAs, with the next step's fragments read at the step's
+// start; the last step starts with the workgroup barrier, after which the
+// wave reads stage kt + 1's first fragments and issues its copies of stage
+// kt + NST into the buffer stage kt leaves (see the loop for why that order
+// is safe).
 template <typename T, typename L, int RB, int NST>
 __device__ __forceinline__ void tile_mainloop_ring(
     f32x16_t (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
@@ -282,50 +277,41 @@ __device__ __forceinline__ void tile_mainloop_ring(
       if (n >= n0 && n < n1) read_one(stage_off, st, buf, n);
   };
 
-  for (int st = 0; st < NST - 1; ++st) {
+  for (int st = 0; st < NST; ++st) {
     stage_offsets(st);
 #pragma unroll
     for (int c = 0; c < P::kCopies; ++c) copy_one(st, c);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm((NST - 2) * P::kCopies, 15));
+  // stage 0 landed (the copies of stages 1 .. NST-1 may stay outstanding)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm((NST - 1) * P::kCopies, 15));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   reads(0, 0, 0, 0, kReads);
   const T* tag = nullptr;
 
-  // Copies are spread evenly over the stage's S * R row groups. With a
-  // 2-deep ring the copies of stage kt + 1 must all be issued before the
-  // barrier of stage kt (which waits for them), so they go into the row
-  // groups up to the last step's first one.
-  constexpr int kGroups = S * R;
-  constexpr int kBarrierGroup = (S - 1) * R;  // group after which we wait
-  constexpr int kSpread = NST >= 3 ? kGroups : kBarrierGroup + 1;
+  // Each step's fragment reads are spread over the previous step's row
+  // groups (A0 and the B fragments first). The last step of stage kt opens
+  // with the barrier, which waits until this wave's copies of stage kt + 1
+  // have landed and its own LDS reads have completed: after it every wave
+  // holds stage kt's fragments in registers, so buffer kt % NST is free and
+  // the wave issues its copies of stage kt + NST into it while reading stage
+  // kt + 1's first fragments. Copies of stages kt + 2 .. kt + NST - 1 may
+  // stay outstanding at the barrier.
+  constexpr int kVmAllowed = (NST - 2) * P::kCopies;
+  static_assert((NST - 1) * P::kCopies <= 63, "vmcnt range");
   auto copies_at = [&](int s, int grp) {
 #pragma unroll
     for (int c = 0; c < P::kCopies; ++c)
-      if (c * kSpread / P::kCopies == grp) copy_one(s, c);
+      if (c * R / P::kCopies == grp) copy_one(s, c);
   };
-  // copies of the newest stage issued by the barrier point; the copies that
-  // may still be outstanding there are those of the stages after kt + 1
-  constexpr int kIssuedByBarrier =
-      (kBarrierGroup + 1) * P::kCopies / kSpread +
-      ((kBarrierGroup + 1) * P::kCopies % kSpread ? 1 : 0);
-  constexpr int kVmAllowed =
-      NST >= 3 ? (NST - 3) * P::kCopies +
-                     (kIssuedByBarrier < P::kCopies ? kIssuedByBarrier
-                                                    : P::kCopies)
-               : 0;
-  static_assert(kVmAllowed <= 63, "vmcnt range");
 
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = (kt % NST) * P::kStageBytes;
     const int nxt = ((kt + 1) % NST) * P::kStageBytes;
-    stage_offsets(kt + NST - 1);
 #pragma unroll
     for (int st = 0; st < S - 1; ++st) {
 #pragma unroll
       for (int q = 0; q < R; ++q) {
-        copies_at(kt + NST - 1, st * R + q);
         reads(cur, st + 1, (st + 1) & 1, q * kReads / R,
               (q + 1) * kReads / R);
         mma_row<C>(acc[q], af[st & 1][q], bfr[st & 1], tag);
@@ -333,17 +319,14 @@ __device__ __forceinline__ void tile_mainloop_ring(
       }
     }
     constexpr int LB = (S - 1) & 1;
-    copies_at(kt + NST - 1, kBarrierGroup);
-    mma_row<C>(acc[0], af[LB][0], bfr[LB], tag);
-    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kVmAllowed, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (R == 1) reads(nxt, 0, 0, 0, kReads);
+    stage_offsets(kt + NST);
 #pragma unroll
-    for (int q = 1; q < R; ++q) {
-      copies_at(kt + NST - 1, kBarrierGroup + q);
-      reads(nxt, 0, 0, (q - 1) * kReads / (R - 1), q * kReads / (R - 1));
+    for (int q = 0; q < R; ++q) {
+      reads(nxt, 0, 0, q * kReads / R, (q + 1) * kReads / R);
+      copies_at(kt + NST, q);
       mma_row<C>(acc[q], af[LB][q], bfr[LB], tag);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -356,7 +339,8 @@ __device__ __forceinline__ void tile_mainloop_ring(
 
 // Build-time shape of the engine (measured on the 1M-context slice: 4 x 2
 // waves with a 4-deep ring of 64-byte slabs is the fastest of the shapes
-// tried; 2 x 2 waves and a 2-deep ring of 128-byte slabs also work).
+// tried; 2 x 2 waves and a 2-deep ring of 128-byte slabs also work, and a
+// 3- or 5-deep ring times the same).
 #ifndef VPCE_WAVES_M
 #define VPCE_WAVES_M 4
 #endif
@@ -371,6 +355,7 @@ __device__ __forceinline__ void tile_mainloop_ring(
 using TileLayout = Layout<VPCE_WAVES_M, 2>;
 constexpr int kThreads = TileLayout::kThreads;
 
+// smem must hold kGemmLds bytes.
 template <typename T>
 __device__ __forceinline__ void tile_mainloop(
     f32x16_t (&acc)[TileLayout::R][TileLayout::C], const T* __restrict__ A,

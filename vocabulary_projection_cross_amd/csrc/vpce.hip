@@ -33,14 +33,18 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kChunkCols = 4096;  // backward chunk width C
+// Backward chunk width C: 64 column tiles, so the dW grid (64 x ceil(d/256)
+// tiles) fills whole waves of 256 workgroups for d a multiple of 1024, and
+// the fp32 read-modify-write of dH happens once per 16384 vocabulary rows.
+constexpr int kChunkCols = 16384;
 constexpr int kMaxSplits = 16;
 constexpr int64_t kMaxTokens = 2000000;
 // Grouped raster (consecutive workgroups of an XCD share operand rows): how
 // many token / output-row tiles sweep the column tiles together. Measured on
 // the 1M-context slice: 2 suits the forward, 8 the backward products.
 constexpr int kGroupFwd = 2;
-constexpr int kGroupBwd = 8;
+constexpr int kGroupBwd = 8;  // the backward's dW and dH products
+constexpr int kGroupRec = 4;  // the backward's logit recompute
 constexpr int kLabIgnored = -2;   // label slot codes in LDS
 constexpr int kLabInvalid = -1;
 using TL = TileLayout;
@@ -348,6 +352,12 @@ __global__ __launch_bounds__(256) void transpose_kernel(
   }
 }
 
+// Transposed G tile staged in LDS (bf16): 256 columns, each 256 tokens long,
+// padded by 16 bytes so that the lanes writing 32 different columns spread
+// over the banks.
+constexpr int kGtColBytes = kTile * 2 + 16;
+constexpr int kGtLds = kTile * kGtColBytes;
+
 struct GParams {
   const void* H;
   const void* Wc;        // first row of the chunk in W
@@ -378,14 +388,17 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c,
 template <typename T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 void recompute_g_kernel(GParams a) {
-  __shared__ __attribute__((aligned(16))) char smem[kGemmLds];
+  // The operand ring, reused after the mainloop as the transposed G tile
+  // (bf16: 256 columns of 256 tokens, padded to kGtColBytes per column).
+  __shared__ __attribute__((aligned(16)))
+  char smem[kGemmLds > kGtLds ? kGemmLds : kGtLds];
   __shared__ __attribute__((aligned(16))) int lab_s[kTile];
   __shared__ __attribute__((aligned(16))) float lse_s[kTile];
 
   const int total = a.T * a.CT;
   const int idx = xcd_remap(blockIdx.x, total);
   int it, ct;
-  grouped_tile(idx, a.T, a.CT, kGroupBwd, it, ct);
+  grouped_tile(idx, a.T, a.CT, kGroupRec, it, ct);
   const int tid = threadIdx.x;
   const int64_t tok0 = (int64_t)it * kTile;
   const int64_t c0 = (int64_t)ct * kTile;
@@ -431,12 +444,69 @@ void recompute_g_kernel(GParams a) {
             gg = scale * (pr - (lab == v ? 1.f : 0.f));
           }
           gv[e] = gg;
-          const int64_t tok = tok0 + rowb + e;
-          if (cstore && tok < a.N) store_elem(G + tok * a.C_pad + c, gg);
+          if constexpr (sizeof(T) == 2) {
+            acc[i][jj][rq * 4 + e] = gg;  // kept for the row-major pass
+          } else {
+            const int64_t tok = tok0 + rowb + e;
+            if (cstore && tok < a.N) store_elem(G + tok * a.C_pad + c, gg);
+          }
         }
-        const int64_t tokb = tok0 + rowb;
-        if (cstore && tokb < a.N_pad)
-          store4(GT + c * a.N_pad + tokb, gv[0], gv[1], gv[2], gv[3]);
+        if constexpr (sizeof(T) == 2) {
+          // column (tile-local) cl, tokens rowb..rowb+3 of the tile
+          const int cl = wn * TL::kWaveCols + jj * 32 + p;
+          store4(reinterpret_cast<T*>(smem + cl * kGtColBytes) + rowb, gv[0],
+                 gv[1], gv[2], gv[3]);
+        } else {
+          const int64_t tokb = tok0 + rowb;
+          if (cstore && tokb < a.N_pad)
+            store4(GT + c * a.N_pad + tokb, gv[0], gv[1], gv[2], gv[3]);
+        }
+      }
+    }
+  }
+  if constexpr (sizeof(T) == 2) {
+    // G^T rows from the transposed tile in LDS: each row of the tile (one
+    // vocabulary column, 256 tokens = 512 bytes) is stored by 32 lanes with
+    // 16-byte stores, coalesced.
+    __syncthreads();
+    constexpr int kChunksPerCol = kTile * 2 / 16;  // 32
+#pragma unroll 4
+    for (int id = tid; id < kTile * kChunksPerCol; id += kThreads) {
+      const int cl = id / kChunksPerCol, u = id % kChunksPerCol;
+      const int64_t c = c0 + cl;
+      const int64_t tokb = tok0 + 8 * u;
+      if (c < a.C_pad && tokb < a.N_pad) {
+        const u32x4_t v =
+            *reinterpret_cast<const u32x4_t*>(smem + cl * kGtColBytes + u * 16);
+        *reinterpret_cast<u32x4_t*>(GT + c * a.N_pad + tokb) = v;
+      }
+    }
+    // G rows: the same tile written row-major (row stride kGtColBytes) from
+    // the values kept in acc, then stored 16 bytes per lane.
+    __syncthreads();
+#pragma unroll
+    for (int jj = 0; jj < TL::C; ++jj) {
+      const int cl = wn * TL::kWaveCols + jj * 32 + p;
+#pragma unroll
+      for (int i = 0; i < TL::R; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int row = wm * TL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h +
+                          (rr & 3);
+          store_elem(reinterpret_cast<T*>(smem + row * kGtColBytes) + cl,
+                     acc[i][jj][rr]);
+        }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int id = tid; id < kTile * kChunksPerCol; id += kThreads) {
+      const int row = id / kChunksPerCol, u = id % kChunksPerCol;
+      const int64_t tok = tok0 + row;
+      const int64_t cc = c0 + 8 * u;
+      if (tok < a.N && cc < a.C_pad) {
+        const u32x4_t v =
+            *reinterpret_cast<const u32x4_t*>(smem + row * kGtColBytes + u * 16);
+        *reinterpret_cast<u32x4_t*>(G + tok * a.C_pad + cc) = v;
       }
     }
   }
