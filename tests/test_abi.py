@@ -92,3 +92,16 @@ def test_device_code_hash_reads_the_built_library():
     h = bench.kernel_code_hash()
     assert len(h) == 16 and int(h, 16) >= 0
     assert bench.kernel_code_hash() == h
+
+
+def test_autograd_wrapper_has_no_host_path():
+    """The differentiable wrapper rejects host tensors instead of computing
+    anything on the CPU."""
+    import torch
+    import vocabulary_projection_cross_amd as vp
+    from vocabulary_projection_cross_amd.autograd import cross_entropy
+    H = torch.zeros((4, 16), dtype=torch.bfloat16, requires_grad=True)
+    W = torch.zeros((10, 16), dtype=torch.bfloat16, requires_grad=True)
+    lab = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(vp.VPCEError):
+        cross_entropy(H, W, lab, 2)

@@ -1,0 +1,151 @@
+"""The autograd wrapper against the direct C-ABI calls it is built from, and
+under activation-checkpoint recompute: the loss and every gradient must be
+the same values, and the tensors saved for the backward must be H, W, the
+labels and lse [N] only (no slice of the N x V logits)."""
+import numpy as np
+import pytest
+import torch
+from torch.utils.checkpoint import checkpoint
+
+import workloads as WL
+from tests.gpu_common import require_gpu, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vp():
+    return require_gpu()
+
+
+def _inputs(N, d, V, R, dtype, seed=0):
+    w = WL.Workload(f"ag_{N}x{d}x{V}x{R}_{dtype}", N, d, V, R, dtype,
+                    w_std=0.05, labels="uniform", ignore_frac=0.05)
+    return to_device(WL.make_inputs(w, seed))
+
+
+def _direct(vp, H, W, lab, R, dloss=None):
+    loss, lse = vp.forward(H, W, lab, R)
+    dl = None if dloss is None else torch.tensor([dloss], dtype=torch.float32,
+                                                 device=H.device)
+    dH, dW = vp.backward(H, W, lab, lse, dl, R)
+    return loss, dH, dW
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_autograd_matches_direct_calls(vp, dtype):
+    from vocabulary_projection_cross_amd.autograd import cross_entropy
+    N, d, V, R = 300, 136, 1000, 3
+    say(f"case autograd N={N} d={d} V={V} R={R} {dtype}")
+    H0, W0, lab = _inputs(N, d, V, R, dtype)
+    loss_d, dH, dW = _direct(vp, H0, W0, lab, R)
+    H = H0.clone().requires_grad_(True)
+    W = W0.clone().requires_grad_(True)
+    loss = cross_entropy(H, W, lab, R)
+    loss.backward()
+    torch.cuda.synchronize()
+    assert loss.dtype == torch.float32 and loss.dim() == 0
+    assert torch.equal(loss.detach(), loss_d)
+    assert H.grad.dtype == H.dtype and W.grad.dtype == W.dtype
+    assert torch.equal(H.grad, dH.to(H.dtype))
+    assert torch.equal(W.grad, dW.to(W.dtype))
+
+
+def test_upstream_gradient_scales_the_gradients(vp):
+    from vocabulary_projection_cross_amd.autograd import cross_entropy
+    N, d, V, R = 257, 72, 515, 2
+    say(f"case autograd upstream x3 N={N} d={d} V={V} R={R}")
+    H0, W0, lab = _inputs(N, d, V, R, "f32", seed=3)
+    _, dH, dW = _direct(vp, H0, W0, lab, R, dloss=3.0)
+    H = H0.clone().requires_grad_(True)
+    W = W0.clone().requires_grad_(True)
+    (3.0 * cross_entropy(H, W, lab, R)).backward()
+    torch.cuda.synchronize()
+    assert torch.equal(H.grad, dH)
+    assert torch.equal(W.grad, dW)
+
+
+def test_only_the_requested_gradient_is_produced(vp):
+    from vocabulary_projection_cross_amd.autograd import cross_entropy
+    N, d, V, R = 300, 64, 700, 2
+    say(f"case autograd W only N={N} d={d} V={V} R={R}")
+    H0, W0, lab = _inputs(N, d, V, R, "bf16", seed=5)
+    _, _, dW = _direct(vp, H0, W0, lab, R)
+    W = W0.clone().requires_grad_(True)
+    cross_entropy(H0, W, lab, R).backward()
+    torch.cuda.synchronize()
+    assert H0.grad is None
+    assert torch.equal(W.grad, dW.to(W.dtype))
+    with torch.no_grad():
+        loss = cross_entropy(H0, W0, lab, R)
+    assert not loss.requires_grad
+
+
+def test_saved_tensors_are_inputs_and_lse_only(vp):
+    from vocabulary_projection_cross_amd.autograd import cross_entropy
+    N, d, V, R = 513, 264, 2049, 2
+    say(f"case autograd saved tensors N={N} d={d} V={V} R={R}")
+    H0, W0, lab = _inputs(N, d, V, R, "bf16", seed=7)
+    H = H0.clone().requires_grad_(True)
+    W = W0.clone().requires_grad_(True)
+    saved = []
+
+    def pack(t):
+        saved.append((tuple(t.shape), t.dtype, t.data_ptr()))
+        return t
+
+    with torch.autograd.graph.saved_tensors_hooks(pack, lambda t: t):
+        loss = cross_entropy(H, W, lab, R)
+    ptrs = {H.data_ptr(), W.data_ptr(), lab.data_ptr()}
+    fresh = [s for s in saved if s[2] not in ptrs]
+    assert len(fresh) == 1, saved
+    assert fresh[0][0] == (N,) and fresh[0][1] == torch.float32
+    loss.backward()
+
+
+def test_checkpoint_recompute_gives_the_same_gradients(vp):
+    from vocabulary_projection_cross_amd.autograd import cross_entropy
+    N, d0, d, V, R = 1024, 64, 256, 4000, 4
+    say(f"case autograd checkpoint N={N} d0={d0} d={d} V={V} R={R}")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x0 = torch.randn((N, d0), device="cuda", generator=g)
+    A0 = torch.randn((d0, d), device="cuda", generator=g) / d0 ** 0.5
+    W0 = (torch.randn((V, d), device="cuda", generator=g) * 0.1).to(
+        torch.bfloat16)
+    lab = torch.randint(0, V, (N,), device="cuda", generator=g)
+    lab[::17] = -100
+
+    def block(x, A, W):
+        H = (x @ A).to(torch.bfloat16)
+        return cross_entropy(H, W, lab, R)
+
+    def run(use_ckpt):
+        x = x0.clone().requires_grad_(True)
+        A = A0.clone().requires_grad_(True)
+        W = W0.clone().requires_grad_(True)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        if use_ckpt:
+            loss = checkpoint(block, x, A, W, use_reentrant=False)
+        else:
+            loss = block(x, A, W)
+        torch.cuda.synchronize()
+        held = torch.cuda.memory_allocated() - base
+        loss.backward()
+        torch.cuda.synchronize()
+        return loss.detach(), x.grad, A.grad, W.grad, held
+
+    run(False)  # first use allocates the BLAS library's own workspace
+    l0, gx0, gA0, gW0, held0 = run(False)
+    l1, gx1, gA1, gW1, held1 = run(True)
+    say(f"bytes held between forward and backward: plain {held0}, "
+        f"checkpointed {held1}")
+    assert torch.equal(l0, l1)
+    assert torch.equal(gW0, gW1)
+    torch.testing.assert_close(gx1, gx0, rtol=1e-6, atol=0)
+    torch.testing.assert_close(gA1, gA0, rtol=1e-6, atol=0)
+    # the plain graph holds H (bf16) and lse, nothing of size V; the
+    # checkpointed one neither (allocator blocks are multiples of 512 bytes)
+    assert held0 - held1 >= N * d * 2 + N * 4
+    assert held0 <= N * d * 2 + N * 4 + 4096
+    assert np.isfinite(float(l0))

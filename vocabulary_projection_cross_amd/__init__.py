@@ -8,6 +8,9 @@ stream. There is no CPU path: if the library is missing, every call raises.
 
     loss, lse = forward(H, W, labels, R)
     dH, dW = backward(H, W, labels, lse, dloss, R)
+
+``vocabulary_projection_cross_amd.autograd.cross_entropy`` wraps the pair as
+a differentiable scalar loss for torch.autograd.
 """
 from __future__ import annotations
 
