@@ -247,6 +247,8 @@ def main():
     loss, lse, dH, dW = step()
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated()
+    requested_peak = torch.cuda.memory_stats()["requested_bytes.all.peak"]
+    planned = vp.plan(w.N, w.d, w.V, w.R, 1 << 62, H.dtype)
     ms = total_ms / args.steps
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -287,6 +289,11 @@ def main():
                              "workspace": int(ws.numel()),
                              "other": int(peak - in_bytes - out_bytes -
                                           ws.numel())},
+        # exact bytes requested from the allocator at the peak (before its
+        # block rounding) and the planner's prediction made before launch;
+        # they differ by the 4-byte upstream-gradient scalar
+        "requested_peak_bytes": int(requested_peak),
+        "planned_peak_bytes": planned["peak_bytes"],
         "roofline": {"bound": "mfma", "kernel": "fwd_lse_kernel",
                      "achieved": fwd_tf, "peak": peak_tf, "unit": "TFLOP/s",
                      "frac": fwd_tf / peak_tf, "traffic": traffic,

@@ -61,19 +61,57 @@ typedef enum {
                                / 4 (f32) */
   VPCE_ERR_UNSUPPORTED = 3, /* unknown dtype */
   VPCE_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
-  VPCE_ERR_WORKSPACE = 5,   /* workspace_bytes < vpce_workspace_bytes(...) */
+  VPCE_ERR_WORKSPACE = 5,   /* workspace too small for the call (see the
+                               workspace notes of each call), or a budget
+                               that cannot hold the operation */
   VPCE_ERR_HIP = 6          /* a kernel launch failed */
 } vpce_status_t;
 
 /*
- * Bytes of device workspace that vpce_forward and vpce_backward need for this
- * shape. Pure host function (no GPU call). The result does not depend on V:
- * the forward keeps per-token partial states for R shards times a fixed number
- * of vocabulary splits, the backward a fixed-width chunk of recomputed
- * logit gradients. Returns 0 for arguments vpce_forward would reject.
+ * Bytes of device workspace that one buffer serving both vpce_forward and
+ * vpce_backward needs for this shape at the widest backward chunk (16384
+ * vocabulary columns). Pure host function (no GPU call). The result does not
+ * depend on V: the forward keeps per-token partial states for R shards times
+ * a fixed number of vocabulary splits, the backward a fixed-width chunk of
+ * recomputed logit gradients. Returns 0 for arguments vpce_forward would
+ * reject.
  */
 size_t vpce_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
                             int32_t dtype);
+
+/*
+ * As vpce_workspace_bytes, for a backward chunk of chunk_cols vocabulary
+ * columns (a multiple of 256 in [256, 16384]; 0 is returned otherwise). The
+ * backward chunk is the memory that stands in for the logit strip of section
+ * 3.2: its gradient chunk G [N x C], G^T and the W chunk^T grow linearly
+ * with C.
+ * Narrower chunks cost more passes of the fp32 dH read-modify-write.
+ */
+size_t vpce_workspace_bytes_chunk(int64_t N, int64_t d, int64_t V, int32_t R,
+                                  int32_t dtype, int64_t chunk_cols);
+
+/*
+ * Byte-budget planner (section 3.2: the strip size is chosen so that it fits
+ * the device; section 4: a configuration's per-device bytes are fixed by the
+ * launch configuration and can be checked before launch). Pure host function.
+ *   budget_bytes     device bytes available to one forward + backward: the
+ *                    caller's buffers (H, W, labels, lse, loss, dH, dW) plus
+ *                    one shared workspace
+ *   chunk_cols       out: the widest backward chunk that fits
+ *   workspace_bytes  out: vpce_workspace_bytes_chunk(..., *chunk_cols)
+ *   peak_bytes       out: exact device bytes live during the backward, the
+ *                    step's peak: the caller's buffers plus the workspace
+ *                    (each buffer at its exact size; an allocator that rounds
+ *                    sizes up adds its own rounding)
+ * R is the ring degree fixed by the parallel layout and is not chosen here:
+ * with the strip never formed, R changes only the forward's per-token partial
+ * states. Returns VPCE_OK, an argument error as vpce_forward would, or
+ * VPCE_ERR_WORKSPACE if even a 256-column chunk does not fit (outputs are
+ * then left untouched).
+ */
+int32_t vpce_plan(int64_t N, int64_t d, int64_t V, int32_t R, int32_t dtype,
+                  size_t budget_bytes, int64_t* chunk_cols,
+                  size_t* workspace_bytes, size_t* peak_bytes);
 
 /*
  * Forward (section 3.2: per-shard strip, online log-sum-exp fold, target logit
@@ -85,7 +123,9 @@ size_t vpce_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
  *   lse      [N]      float32     out: log-sum-exp of every token's logits
  *                                 (ignored tokens included); this is the
  *                                 normaliser the backward pass needs
- *   workspace, workspace_bytes    scratch of at least vpce_workspace_bytes()
+ *   workspace, workspace_bytes    scratch; the forward uses only its part,
+ *                                 which any buffer of at least
+ *                                 vpce_workspace_bytes_chunk(..., 256) holds
  *   stream                        hipStream_t to enqueue on
  * Returns VPCE_OK or an error status (nothing enqueued on argument errors).
  */
@@ -106,9 +146,14 @@ int32_t vpce_forward(const void* H, const void* W, const int64_t* labels,
  *                                 the device (NULL means 1.0)
  *   dH       [N x d]  float32     out, overwritten: dloss/n_valid * G W
  *   dW       [V x d]  float32     out, overwritten: dloss/n_valid * G^T H
+ *   workspace, workspace_bytes    scratch: the backward runs with the widest
+ *                                 chunk whose backward part fits (at least
+ *                                 the 256-column one, else
+ *                                 VPCE_ERR_WORKSPACE)
  * with G_ij = valid_i * (exp(z_ij - lse_i) - [j == y_i]). The token count
  * n_valid is recounted from labels. Rows of dH for ignored tokens are exactly
- * zero. Results are bitwise reproducible for a fixed shape (no atomics).
+ * zero. Results are bitwise reproducible for a fixed shape and workspace size
+ * (no atomics); the chunk width changes only the fp32 summation order of dH.
  */
 int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
                       const float* lse, const float* dloss, int64_t N,

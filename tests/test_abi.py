@@ -29,8 +29,9 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert names == ["vpce_backward", "vpce_forward", "vpce_status_string",
-                     "vpce_workspace_bytes"]
+    assert names == ["vpce_backward", "vpce_forward", "vpce_plan",
+                     "vpce_status_string", "vpce_workspace_bytes",
+                     "vpce_workspace_bytes_chunk"]
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {vp.library_path()}").read()
@@ -105,3 +106,57 @@ def test_autograd_wrapper_has_no_host_path():
     lab = torch.zeros(4, dtype=torch.int64)
     with pytest.raises(vp.VPCEError):
         cross_entropy(H, W, lab, 2)
+
+
+def _caller_bytes(N, d, V, esz):
+    """H, W, labels, lse, loss, dH, dW at their exact sizes."""
+    return N * d * esz + V * d * esz + 8 * N + 4 * N + 4 + 4 * N * d + 4 * V * d
+
+
+@pytest.mark.parametrize("N,d,V,R", [(65536, 7168, 129280, 8),
+                                     (4096, 2048, 32000, 4), (300, 136, 1000, 3)])
+def test_chunk_workspace_grows_with_the_chunk(lib, N, d, V, R):
+    full = lib.vpce_workspace_bytes(N, d, V, R, 0)
+    assert lib.vpce_workspace_bytes_chunk(N, d, V, R, 0, 16384) == full
+    sizes = [lib.vpce_workspace_bytes_chunk(N, d, V, R, 0, c)
+             for c in range(256, 16385, 256)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+    assert sizes[0] < sizes[-1]
+    for bad in (0, 128, 255, 300, 16640, -256):
+        assert lib.vpce_workspace_bytes_chunk(N, d, V, R, 0, bad) == 0
+
+
+@pytest.mark.parametrize("N,d,V,R,dt", [(65536, 7168, 129280, 8, 0),
+                                        (4096, 2048, 32000, 4, 0),
+                                        (300, 136, 1000, 3, 1)])
+def test_planner_picks_the_widest_chunk_that_fits(N, d, V, R, dt):
+    import torch
+    dtype = torch.bfloat16 if dt == 0 else torch.float32
+    esz = 2 if dt == 0 else 4
+    fixed = _caller_bytes(N, d, V, esz)
+    for C in (256, 4096, 12800, 16384):
+        ws = vp.workspace_bytes(N, d, V, R, dtype, chunk_cols=C)
+        exact = vp.plan(N, d, V, R, fixed + ws, dtype)
+        assert exact == {"chunk_cols": C, "workspace_bytes": ws,
+                         "peak_bytes": fixed + ws}
+        if C > 256:
+            below = vp.plan(N, d, V, R, fixed + ws - 1, dtype)
+            assert below["chunk_cols"] < C
+            assert below["peak_bytes"] <= fixed + ws - 1
+    roomy = vp.plan(N, d, V, R, 1 << 50, dtype)
+    assert roomy["chunk_cols"] == 16384
+    assert roomy["workspace_bytes"] == vp.workspace_bytes(N, d, V, R, dtype)
+    ws256 = vp.workspace_bytes(N, d, V, R, dtype, chunk_cols=256)
+    with pytest.raises(vp.VPCEError, match="status 5"):
+        vp.plan(N, d, V, R, fixed + ws256 - 1, dtype)
+
+
+def test_planner_argument_errors(lib):
+    c, w, pk = ctypes.c_int64(-7), ctypes.c_size_t(3), ctypes.c_size_t(4)
+    assert lib.vpce_plan(10, 12, 100, 1, 0, 1 << 40, ctypes.byref(c),
+                         ctypes.byref(w), ctypes.byref(pk)) == 2   # d % 8
+    assert lib.vpce_plan(10, 16, 100, 1, 0, 1 << 40, None, ctypes.byref(w),
+                         ctypes.byref(pk)) == 1
+    assert lib.vpce_plan(10, 16, 100, 1, 0, 100, ctypes.byref(c),
+                         ctypes.byref(w), ctypes.byref(pk)) == 5
+    assert (c.value, w.value, pk.value) == (-7, 3, 4)   # left untouched

@@ -229,3 +229,68 @@ def test_workspace_is_independent_of_v(vp):
     slack = 2 << 20
     assert all(abs(e - extra[0]) <= slack for e in extra), extra
     assert all(e <= ws + slack for e in extra), (extra, ws)
+
+
+def test_narrow_workspace_runs_ragged_chunks(vp):
+    """A workspace sized for 768-column backward chunks: each 2500-wide shard
+    runs as 768, 768, 768, 196. dW rows come out of one chunk each (bitwise
+    equal to the full-width run); dH sums the chunks in another grouping."""
+    w = WL.Workload("narrow_chunks", N=2048, d=256, V=5000, R=2, dtype="bf16",
+                    w_std=0.05, labels="zipf", zipf_s=1.1, ignore_frac=0.03)
+    say(f"case {w.name} N={w.N} d={w.d} V={w.V} R={w.R} chunk 768")
+    inp = WL.make_inputs(w, 4)
+    H, W, lab = to_device(inp)
+    full = run_gpu(vp, H, W, lab, w.R)
+    ws = torch.empty(vp.workspace_bytes(w.N, w.d, w.V, w.R, H.dtype,
+                                        chunk_cols=768),
+                     dtype=torch.uint8, device=H.device)
+    assert ws.numel() < vp.workspace_bytes(w.N, w.d, w.V, w.R, H.dtype)
+    loss, lse = vp.forward(H, W, lab, w.R, workspace=ws)
+    dH, dW = vp.backward(H, W, lab, lse, None, w.R, workspace=ws)
+    torch.cuda.synchronize()
+    dH = dH.cpu().numpy().astype(np.float64)
+    dW = dW.cpu().numpy().astype(np.float64)
+    assert float(loss.item()) == full[0]
+    assert np.array_equal(lse.cpu().numpy().astype(np.float64), full[1])
+    assert np.array_equal(dW, full[3])
+    assert np.abs(dH - full[2]).max() <= 1e-6 * np.abs(full[2]).max()
+    Hf, Wf = inp.H_f64(), inp.W_f64()
+    rdH, rdW = oracle.backward(Hf, Wf, inp.labels, 1.0)
+    okH, eH = C.grad_ok(dH, rdH)
+    okW, eW = C.grad_ok(dW, rdW)
+    say(C.report(w.name, dH_maxabs=eH[0], dH_ref=eH[1], dH_cos=eH[2],
+                 dW_maxabs=eW[0], dW_ref=eW[1], dW_cos=eW[2]))
+    assert okH, eH
+    assert okW, eW
+
+
+def test_planned_peak_is_the_measured_peak(vp):
+    """The planner's peak, known before launch, against the exact bytes the
+    allocator handed out during one forward + backward (requested sizes,
+    before the allocator's own rounding)."""
+    N, d, V, R = 4096, 1024, 32000, 4
+    fixed = (N * d * 2 + V * d * 2 + 8 * N) + (4 * N + 4 + 4 * N * d
+                                               + 4 * V * d)
+    budget = fixed + vp.workspace_bytes(N, d, V, R, torch.bfloat16,
+                                        chunk_cols=2048)
+    plan = vp.plan(N, d, V, R, budget)
+    say(f"case planned peak N={N} d={d} V={V} R={R} plan={plan}")
+    assert plan["chunk_cols"] == 2048 and plan["peak_bytes"] == budget
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_stats()["requested_bytes.all.current"]
+    g = torch.Generator(device="cuda").manual_seed(2)
+    H = torch.randn((N, d), device="cuda", generator=g).to(torch.bfloat16)
+    W = (torch.randn((V, d), device="cuda", generator=g) * 0.03).to(
+        torch.bfloat16)
+    lab = torch.randint(0, V, (N,), device="cuda", generator=g)
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    loss, lse = vp.forward(H, W, lab, R, workspace=ws)
+    dH, dW = vp.backward(H, W, lab, lse, None, R, workspace=ws)
+    torch.cuda.synchronize()
+    peak = torch.cuda.memory_stats()["requested_bytes.all.peak"] - base
+    say(f"planned {plan['peak_bytes']} measured {peak}")
+    assert peak == plan["peak_bytes"]
+    assert math.isfinite(float(loss.item()))

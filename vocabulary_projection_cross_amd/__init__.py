@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["forward", "backward", "workspace_bytes", "VPCEError",
+__all__ = ["forward", "backward", "workspace_bytes", "plan", "VPCEError",
            "library_path", "IGNORE_INDEX", "VPCE_BF16", "VPCE_F32"]
 
 IGNORE_INDEX = -100
@@ -53,6 +53,12 @@ def _load():
         ctypes.c_size_t
     lib.vpce_workspace_bytes.restype = sz
     lib.vpce_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    lib.vpce_workspace_bytes_chunk.restype = sz
+    lib.vpce_workspace_bytes_chunk.argtypes = [i64, i64, i64, i32, i32, i64]
+    lib.vpce_plan.restype = i32
+    lib.vpce_plan.argtypes = [i64, i64, i64, i32, i32, sz,
+                              ctypes.POINTER(i64), ctypes.POINTER(sz),
+                              ctypes.POINTER(sz)]
     lib.vpce_forward.restype = i32
     lib.vpce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i32,
                                  vp, vp, vp, sz, vp]
@@ -104,19 +110,49 @@ def _validate(H, W, labels):
 
 
 def workspace_bytes(N: int, d: int, V: int, R: int,
-                    dtype: torch.dtype = torch.bfloat16) -> int:
-    return int(_load().vpce_workspace_bytes(N, d, V, R, _dtype_code(dtype)))
+                    dtype: torch.dtype = torch.bfloat16,
+                    chunk_cols: Optional[int] = None) -> int:
+    """Workspace bytes for forward + backward (0 for invalid arguments): at
+    the widest backward chunk, or at chunk_cols (a multiple of 256 in
+    [256, 16384])."""
+    if chunk_cols is None:
+        return int(_load().vpce_workspace_bytes(N, d, V, R,
+                                                _dtype_code(dtype)))
+    return int(_load().vpce_workspace_bytes_chunk(N, d, V, R,
+                                                  _dtype_code(dtype),
+                                                  chunk_cols))
+
+
+def plan(N: int, d: int, V: int, R: int, budget_bytes: int,
+         dtype: torch.dtype = torch.bfloat16) -> dict:
+    """The widest backward chunk whose step fits in budget_bytes of device
+    memory (the caller's inputs and outputs plus one shared workspace), with
+    the workspace size and the exact peak device bytes of a forward +
+    backward step, known before anything is launched."""
+    lib = _load()
+    c = ctypes.c_int64(0)
+    ws = ctypes.c_size_t(0)
+    peak = ctypes.c_size_t(0)
+    _check(lib.vpce_plan(N, d, V, R, _dtype_code(dtype), budget_bytes,
+                         ctypes.byref(c), ctypes.byref(ws),
+                         ctypes.byref(peak)))
+    return {"chunk_cols": int(c.value), "workspace_bytes": int(ws.value),
+            "peak_bytes": int(peak.value)}
 
 
 def _workspace(H, W, R, workspace):
+    """The caller's workspace (the library checks that it is large enough
+    and fits the backward chunk to it), or a new one of the full size."""
+    if workspace is not None:
+        if (workspace.device != H.device or not workspace.is_contiguous()
+                or workspace.dtype != torch.uint8):
+            raise VPCEError("workspace must be a contiguous uint8 tensor on "
+                            "H's device")
+        return workspace
     need = workspace_bytes(H.shape[0], H.shape[1], W.shape[0], R, H.dtype)
     if need == 0:
         raise VPCEError("invalid shape for the vocabulary-projection CE")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
-    elif workspace.numel() * workspace.element_size() < need:
-        raise VPCEError(f"workspace too small: need {need} bytes")
-    return workspace
+    return torch.empty(need, dtype=torch.uint8, device=H.device)
 
 
 def forward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, R: int,

@@ -33,10 +33,13 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Backward chunk width C: 64 column tiles, so the dW grid (64 x ceil(d/256)
-// tiles) fills whole waves of 256 workgroups for d a multiple of 1024, and
-// the fp32 read-modify-write of dH happens once per 16384 vocabulary rows.
+// Backward chunk width C: at most 64 column tiles, so the dW grid
+// (64 x ceil(d/256) tiles) fills whole waves of 256 workgroups for d a
+// multiple of 1024, and the fp32 read-modify-write of dH happens once per
+// 16384 vocabulary rows. A smaller workspace gets the widest multiple of
+// kChunkStep that fits.
 constexpr int kChunkCols = 16384;
+constexpr int kChunkStep = 256;
 constexpr int kMaxSplits = 16;
 constexpr int64_t kMaxTokens = 2000000;
 // Grouped raster (consecutive workgroups of an XCD share operand rows): how
@@ -615,7 +618,8 @@ int32_t check_shape(int64_t N, int64_t d, int64_t V, int32_t R, int32_t dt) {
   return VPCE_OK;
 }
 
-Plan make_plan(int64_t N, int64_t d, int64_t V, int R, int dt) {
+Plan make_plan(int64_t N, int64_t d, int64_t V, int R, int dt,
+               int64_t C = kChunkCols) {
   Plan p{};
   p.N = N; p.d = d; p.V = V; p.R = R; p.dt = dt;
   p.esz = dt == VPCE_BF16 ? 2 : 4;
@@ -623,7 +627,7 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int R, int dt) {
   p.S = splits_for(p.T > 0 ? p.T : 1, R);
   p.nb = (int)((N + 255) / 256);
   p.N_pad = (N + 63) / 64 * 64;
-  p.C = kChunkCols;
+  p.C = C;
   size_t o = 0;
   const size_t part = (size_t)R * p.S * (size_t)N * 4;
   p.o_pm = o; o = up(o + part);
@@ -641,6 +645,31 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int R, int dt) {
   p.bwd_bytes = o;
   p.bytes = p.fwd_bytes > p.bwd_bytes ? p.fwd_bytes : p.bwd_bytes;
   return p;
+}
+
+bool valid_chunk(int64_t C) {
+  return C >= kChunkStep && C <= kChunkCols && C % kChunkStep == 0;
+}
+
+// The widest backward chunk whose workspace fits in `bytes` (0 if even the
+// narrowest does not): the backward's own part, or (shared) the buffer that
+// serves the forward and the backward. Both grow with C, so the first width
+// that fits, scanning down, is the widest.
+int64_t widest_chunk(int64_t N, int64_t d, int64_t V, int R, int dt,
+                     size_t bytes, bool shared) {
+  for (int64_t C = kChunkCols; C >= kChunkStep; C -= kChunkStep) {
+    const Plan p = make_plan(N, d, V, R, dt, C);
+    if ((shared ? p.bytes : p.bwd_bytes) <= bytes) return C;
+  }
+  return 0;
+}
+
+// Device bytes of the caller's own buffers around one forward + backward:
+// inputs H, W, labels; outputs lse, loss, dH, dW.
+size_t caller_bytes(int64_t N, int64_t d, int64_t V, int dt) {
+  const size_t esz = dt == VPCE_BF16 ? 2 : 4;
+  return (size_t)N * d * esz + (size_t)V * d * esz + (size_t)N * 8 +
+         (size_t)N * 4 + 4 + (size_t)N * d * 4 + (size_t)V * d * 4;
 }
 
 inline bool aligned(const void* p, size_t a) {
@@ -757,6 +786,32 @@ size_t vpce_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
   return make_plan(N, d, V, R, dtype).bytes;
 }
 
+size_t vpce_workspace_bytes_chunk(int64_t N, int64_t d, int64_t V, int32_t R,
+                                  int32_t dtype, int64_t chunk_cols) {
+  if (check_shape(N, d, V, R, dtype) != VPCE_OK || !valid_chunk(chunk_cols))
+    return 0;
+  return make_plan(N, d, V, R, dtype, chunk_cols).bytes;
+}
+
+int32_t vpce_plan(int64_t N, int64_t d, int64_t V, int32_t R, int32_t dtype,
+                  size_t budget_bytes, int64_t* chunk_cols,
+                  size_t* workspace_bytes, size_t* peak_bytes) {
+  const int32_t s = check_shape(N, d, V, R, dtype);
+  if (s != VPCE_OK) return s;
+  if (!chunk_cols || !workspace_bytes || !peak_bytes) return VPCE_ERR_NULL;
+  const size_t fixed = caller_bytes(N, d, V, dtype);
+  const int64_t C =
+      budget_bytes > fixed
+          ? widest_chunk(N, d, V, R, dtype, budget_bytes - fixed, true)
+          : 0;
+  if (C == 0) return VPCE_ERR_WORKSPACE;
+  const size_t ws = make_plan(N, d, V, R, dtype, C).bytes;
+  *chunk_cols = C;
+  *workspace_bytes = ws;
+  *peak_bytes = fixed + ws;
+  return VPCE_OK;
+}
+
 int32_t vpce_forward(const void* H, const void* W, const int64_t* labels,
                      int64_t N, int64_t d, int64_t V, int32_t R,
                      int64_t ignore_index, int32_t dtype, float* loss,
@@ -770,7 +825,7 @@ int32_t vpce_forward(const void* H, const void* W, const int64_t* labels,
       !aligned(loss, 4) || (lse && !aligned(lse, 4)) || !aligned(workspace, kAlign))
     return VPCE_ERR_ALIGN;
   const Plan p = make_plan(N, d, V, R, dtype);
-  if (workspace_bytes < p.bytes) return VPCE_ERR_WORKSPACE;
+  if (workspace_bytes < p.fwd_bytes) return VPCE_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == VPCE_BF16)
@@ -791,8 +846,9 @@ int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
       (lse && !aligned(lse, 4)) || (dloss && !aligned(dloss, 4)) ||
       (dH && !aligned(dH, 4)) || !aligned(dW, 4) || !aligned(workspace, kAlign))
     return VPCE_ERR_ALIGN;
-  const Plan p = make_plan(N, d, V, R, dtype);
-  if (workspace_bytes < p.bytes) return VPCE_ERR_WORKSPACE;
+  const int64_t C = widest_chunk(N, d, V, R, dtype, workspace_bytes, false);
+  if (C == 0) return VPCE_ERR_WORKSPACE;
+  const Plan p = make_plan(N, d, V, R, dtype, C);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == VPCE_BF16)
