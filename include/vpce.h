@@ -161,6 +161,100 @@ int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
                       int32_t dtype, float* dH, float* dW, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * ---- Shard-level calls: one batch meets one vocabulary shard --------------
+ *
+ * Ring-DTP moves either the activations or the weight shard around the ring
+ * (section 3.2 and Figure 9 of the paper above); the gradient of the moving
+ * tensor travels with it. vpce_forward / vpce_backward run the move-weights
+ * order for one rank on one device. The calls below are the per-hop steps of
+ * either order: a batch (H, labels) carries a running per-token state from
+ * shard to shard, then its lse, then its dH, while each shard keeps its dW.
+ *
+ * The running state of a batch is 3 x N floats, [m | s | t], base 2:
+ *   m_i = log2(e) * max over the logits z_ij seen so far (-inf before any),
+ *   s_i = sum over those logits of 2^(log2(e) * z_ij - m_i)   (0 before any),
+ *   t_i = the target logit z_{i,y_i} once its shard has been folded (NaN
+ *         before, and for ignored or out-of-range labels).
+ * After every shard has been folded, lse_i = ln 2 * (m_i + log2 s_i). The fold
+ * order changes results only through fp32 rounding.
+ *
+ * The loss over several batches is a mean over all their tokens: each
+ * finished batch adds (sum of its token losses, its valid-token count) to a
+ * running fp64 pair `totals` (a ring of devices all-reduces that pair), and
+ * the backward of every batch scales G by dloss / totals[1].
+ *
+ * Workspace: any buffer of at least vpce_workspace_bytes(N, d, V, 1, dtype)
+ * bytes serves every shard-level call for that batch (the backward fits its
+ * chunk to the buffer as vpce_backward does).
+ */
+
+/* Which tensor a ring of R ranks sends per hop. */
+typedef enum {
+  VPCE_RING_MOVE_WEIGHTS = 0,     /* shards travel, batches stay */
+  VPCE_RING_MOVE_ACTIVATIONS = 1  /* batches travel, shards stay */
+} vpce_ring_mode_t;
+
+/*
+ * The cheaper direction for a ring of R ranks with N tokens each (section
+ * 3.2: the bytes sent per hop are N*d*b if activations move and (V/R)*d*b if
+ * weights move; weights move exactly when the shard is the smaller, i.e. when
+ * the widest shard ceil(V/R) has fewer rows than the batch has tokens). Pure
+ * host function. Writes the mode and both per-hop payloads in bytes.
+ */
+int32_t vpce_ring_mode(int64_t N, int64_t d, int64_t V, int32_t R,
+                       int32_t dtype, int32_t* mode, size_t* activation_bytes,
+                       size_t* weight_bytes);
+
+/* state [3 x N] = [-inf | 0 | NaN]: the empty running state of a batch. */
+int32_t vpce_state_init(float* state, int64_t N, void* stream);
+
+/*
+ * Fold one shard into a batch's running state.
+ *   H        [N x d]        dtype   the batch's hidden states
+ *   W_shard  [v_count x d]  dtype   rows v_begin .. v_begin + v_count - 1 of W
+ *   labels   [N]            int64   the batch's targets, vocabulary indices in
+ *                                   [0, V) (or ignore_index)
+ *   V                               size of the whole vocabulary
+ *   state    [3 x N]        float32 in/out, as defined above
+ * Requires 0 <= v_begin, 1 <= v_count, v_begin + v_count <= V, and the
+ * conventions of vpce_forward for everything else.
+ */
+int32_t vpce_shard_fold(const void* H, const void* W_shard,
+                        const int64_t* labels, int64_t N, int64_t d, int64_t V,
+                        int64_t v_begin, int64_t v_count,
+                        int64_t ignore_index, int32_t dtype, float* state,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Close a batch whose state has seen every shard: write lse [N] (for every
+ * token), add (sum of its valid tokens' losses lse_i - t_i, its valid-token
+ * count) to totals [2] (fp64, in/out, the caller zeroes it before the first
+ * batch), and, when loss is not NULL, write the mean over everything in
+ * totals so far (0 if no valid token). A valid token with an out-of-range
+ * label has t = NaN, so the loss is NaN, as in vpce_forward.
+ */
+int32_t vpce_state_finish(const float* state, const int64_t* labels,
+                          int64_t N, int64_t ignore_index, float* lse,
+                          double* totals, float* loss, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of one (batch, shard) meeting: recompute the shard's logits from
+ * the batch's lse, G = (dloss / totals[1]) * valid * (softmax - onehot), and
+ * ACCUMULATE dH += G W_shard and dW_shard += G^T H (both fp32; the caller
+ * zeroes them before the first meeting). dloss [1] on the device, NULL = 1.
+ * Same arguments and requirements as vpce_shard_fold otherwise.
+ */
+int32_t vpce_shard_backward(const void* H, const void* W_shard,
+                            const int64_t* labels, const float* lse,
+                            const double* totals, const float* dloss,
+                            int64_t N, int64_t d, int64_t V, int64_t v_begin,
+                            int64_t v_count, int64_t ignore_index,
+                            int32_t dtype, float* dH, float* dW_shard,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* vpce_status_string(int32_t status);
 

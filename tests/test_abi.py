@@ -30,8 +30,10 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = header_functions()
     assert names == ["vpce_backward", "vpce_forward", "vpce_plan",
-                     "vpce_status_string", "vpce_workspace_bytes",
-                     "vpce_workspace_bytes_chunk"]
+                     "vpce_ring_mode", "vpce_shard_backward",
+                     "vpce_shard_fold", "vpce_state_finish",
+                     "vpce_state_init", "vpce_status_string",
+                     "vpce_workspace_bytes", "vpce_workspace_bytes_chunk"]
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {vp.library_path()}").read()
@@ -160,3 +162,61 @@ def test_planner_argument_errors(lib):
     assert lib.vpce_plan(10, 16, 100, 1, 0, 100, ctypes.byref(c),
                          ctypes.byref(w), ctypes.byref(pk)) == 5
     assert (c.value, w.value, pk.value) == (-7, 3, 4)   # left untouched
+
+
+def test_ring_mode_rule_on_the_workloads():
+    """Weights move exactly when the widest shard has fewer rows than the
+    batch has tokens; the payloads are N*d*b and ceil(V/R)*d*b."""
+    import torch
+    import workloads as WL
+    modes = {}
+    for w in WL.WORKLOADS:
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        esz = 2 if w.dtype == "bf16" else 4
+        m = vp.ring_mode(w.N, w.d, w.V, w.R, dt)
+        widest = -(-w.V // w.R)
+        assert m["activation_bytes"] == w.N * w.d * esz
+        assert m["weight_bytes"] == widest * w.d * esz
+        modes[w.name] = m["mode"]
+        assert m["mode"] == (vp.MOVE_WEIGHTS if widest < w.N
+                             else vp.MOVE_ACTIVATIONS)
+    # the 4096-token workload has 8000-row shards: its batches travel
+    assert sorted(modes.values()).count(vp.MOVE_ACTIVATIONS) == 2
+    assert vp.ring_mode(100, 8, 1000, 10)["mode"] == vp.MOVE_ACTIVATIONS
+    assert vp.ring_mode(101, 8, 1000, 10)["mode"] == vp.MOVE_WEIGHTS
+
+
+def test_shard_calls_reject_bad_arguments(lib):
+    A = 1 << 20   # aligned fake addresses: never dereferenced on error paths
+    fold = lambda **k: lib.vpce_shard_fold(
+        k.get("H", A), k.get("W", A), A, 4, 16, 10, k.get("vb", 0),
+        k.get("vc", 5), -100, 0, k.get("st", A), A, k.get("wsb", 1 << 20),
+        None)
+    assert fold(vb=6, vc=5) == 2          # past the vocabulary
+    assert fold(vb=-1) == 2
+    assert fold(vc=0) == 2
+    assert fold(W=None) == 1
+    assert fold(st=None) == 1
+    assert fold(H=A + 8) == 4
+    assert fold(wsb=16) == 5
+    assert lib.vpce_state_init(None, 4, None) == 1
+    assert lib.vpce_state_init(None, -1, None) == 2
+    assert lib.vpce_state_init(None, 0, None) == 0   # nothing to do
+    assert lib.vpce_state_finish(A, A, 4, -100, A, None, None, A, 1 << 20,
+                                 None) == 1          # totals
+    assert lib.vpce_state_finish(A, A, 4, -100, A, A + 4, None, A, 1 << 20,
+                                 None) == 4          # totals fp64-aligned
+    assert lib.vpce_state_finish(A, A, 4, -100, A, A, None, A, 8,
+                                 None) == 5
+    bwd = lambda **k: lib.vpce_shard_backward(
+        A, A, A, A, k.get("tot", A), None, 4, 16, 10, k.get("vb", 2), 5,
+        -100, 0, A, k.get("dW", A), A, k.get("wsb", 1 << 20), None)
+    assert bwd(vb=6) == 2
+    assert bwd(tot=None) == 1
+    assert bwd(dW=None) == 1
+    assert bwd(wsb=64) == 5
+    mode, act, wts = ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.vpce_ring_mode(4, 12, 10, 1, 0, ctypes.byref(mode),
+                              ctypes.byref(act), ctypes.byref(wts)) == 2
+    assert lib.vpce_ring_mode(4, 16, 10, 2, 0, None, ctypes.byref(act),
+                              ctypes.byref(wts)) == 1

@@ -20,12 +20,16 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["forward", "backward", "workspace_bytes", "plan", "VPCEError",
-           "library_path", "IGNORE_INDEX", "VPCE_BF16", "VPCE_F32"]
+__all__ = ["forward", "backward", "workspace_bytes", "plan", "ring_mode",
+           "state_init", "shard_fold", "state_finish", "shard_backward",
+           "VPCEError", "library_path", "IGNORE_INDEX", "VPCE_BF16",
+           "VPCE_F32", "MOVE_WEIGHTS", "MOVE_ACTIVATIONS"]
 
 IGNORE_INDEX = -100
 VPCE_BF16 = 0
 VPCE_F32 = 1
+MOVE_WEIGHTS = 0
+MOVE_ACTIVATIONS = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBPATH = os.path.join(_HERE, "libvpce.so")
@@ -65,6 +69,21 @@ def _load():
     lib.vpce_backward.restype = i32
     lib.vpce_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64,
                                   i32, vp, vp, vp, sz, vp]
+    lib.vpce_ring_mode.restype = i32
+    lib.vpce_ring_mode.argtypes = [i64, i64, i64, i32, i32,
+                                   ctypes.POINTER(i32), ctypes.POINTER(sz),
+                                   ctypes.POINTER(sz)]
+    lib.vpce_state_init.restype = i32
+    lib.vpce_state_init.argtypes = [vp, i64, vp]
+    lib.vpce_shard_fold.restype = i32
+    lib.vpce_shard_fold.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                    i32, vp, vp, sz, vp]
+    lib.vpce_state_finish.restype = i32
+    lib.vpce_state_finish.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, sz,
+                                      vp]
+    lib.vpce_shard_backward.restype = i32
+    lib.vpce_shard_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                        i64, i64, i64, i32, vp, vp, vp, sz, vp]
     lib.vpce_status_string.restype = ctypes.c_char_p
     lib.vpce_status_string.argtypes = [i32]
     _lib = lib
@@ -210,3 +229,126 @@ def backward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
                                _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
     _check(st)
     return dH, dW
+
+
+# ---- shard-level calls: one batch meets one vocabulary shard ---------------
+
+def ring_mode(N: int, d: int, V: int, R: int,
+              dtype: torch.dtype = torch.bfloat16) -> dict:
+    """Which tensor a ring of R ranks with N tokens each sends per hop
+    (MOVE_WEIGHTS or MOVE_ACTIVATIONS) and both per-hop payloads in bytes."""
+    lib = _load()
+    mode = ctypes.c_int32(-1)
+    act = ctypes.c_size_t(0)
+    wts = ctypes.c_size_t(0)
+    _check(lib.vpce_ring_mode(N, d, V, R, _dtype_code(dtype),
+                              ctypes.byref(mode), ctypes.byref(act),
+                              ctypes.byref(wts)))
+    return {"mode": int(mode.value), "activation_bytes": int(act.value),
+            "weight_bytes": int(wts.value)}
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _shard_workspace(H, V, workspace):
+    if workspace is not None:
+        return workspace
+    need = workspace_bytes(H.shape[0], H.shape[1], V, 1, H.dtype)
+    if need == 0:
+        raise VPCEError("invalid shape for the vocabulary-projection CE")
+    return torch.empty(need, dtype=torch.uint8, device=H.device)
+
+
+def _check_state(state, N, device):
+    if (state.device != device or state.dtype != torch.float32
+            or state.numel() != 3 * N or not state.is_contiguous()):
+        raise VPCEError("state must be a contiguous fp32 [3, N] tensor on H's "
+                        "device")
+
+
+def state_init(N: int, device) -> torch.Tensor:
+    """A new empty running state [3, N] (m = -inf, s = 0, t = NaN)."""
+    state = torch.empty((3, N), dtype=torch.float32, device=device)
+    with torch.cuda.device(state.device):
+        _check(_load().vpce_state_init(_ptr(state), N, _stream(state)))
+    return state
+
+
+def shard_fold(H: torch.Tensor, W_shard: torch.Tensor, labels: torch.Tensor,
+               V: int, v_begin: int, state: torch.Tensor,
+               ignore_index: int = IGNORE_INDEX,
+               workspace: Optional[torch.Tensor] = None) -> None:
+    """Fold vocabulary rows [v_begin, v_begin + len(W_shard)) into the
+    batch's running state, in place."""
+    _validate(H, W_shard, labels)
+    N, d = H.shape
+    _check_state(state, N, H.device)
+    ws = _shard_workspace(H, V, workspace)
+    with torch.cuda.device(H.device):
+        st = _load().vpce_shard_fold(
+            _ptr(H), _ptr(W_shard), _ptr(labels), N, d, V, v_begin,
+            W_shard.shape[0], ignore_index, _dtype_code(H.dtype), _ptr(state),
+            _ptr(ws), ws.numel(), _stream(H))
+    _check(st)
+
+
+def state_finish(state: torch.Tensor, labels: torch.Tensor,
+                 totals: torch.Tensor, ignore_index: int = IGNORE_INDEX,
+                 workspace: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Close a batch that has met every shard: returns lse [N] and the mean
+    loss over every batch accumulated into totals (fp64 [2], in place)."""
+    N = labels.shape[0]
+    _check_state(state, N, labels.device)
+    if (totals.device != labels.device or totals.dtype != torch.float64
+            or totals.numel() != 2):
+        raise VPCEError("totals must be an fp64 [2] tensor on the device")
+    if labels.dtype != torch.int64 or not labels.is_contiguous():
+        raise VPCEError("labels must be contiguous int64")
+    lse = torch.empty(N, dtype=torch.float32, device=labels.device)
+    loss = torch.empty((), dtype=torch.float32, device=labels.device)
+    ws = workspace if workspace is not None else torch.empty(
+        4096 + 16 * N, dtype=torch.uint8, device=labels.device)
+    with torch.cuda.device(labels.device):
+        st = _load().vpce_state_finish(
+            _ptr(state), _ptr(labels), N, ignore_index, _ptr(lse),
+            _ptr(totals), _ptr(loss), _ptr(ws), ws.numel(), _stream(labels))
+    _check(st)
+    return lse, loss
+
+
+def shard_backward(H: torch.Tensor, W_shard: torch.Tensor,
+                   labels: torch.Tensor, lse: torch.Tensor,
+                   totals: torch.Tensor, dloss: Optional[torch.Tensor],
+                   V: int, v_begin: int, dH: torch.Tensor,
+                   dW_shard: torch.Tensor, ignore_index: int = IGNORE_INDEX,
+                   workspace: Optional[torch.Tensor] = None) -> None:
+    """Accumulate one (batch, shard) meeting's gradients into dH [N, d] and
+    dW_shard [len(W_shard), d] (fp32, in place)."""
+    _validate(H, W_shard, labels)
+    N, d = H.shape
+    for name, t, shape in (("dH", dH, (N, d)),
+                           ("dW_shard", dW_shard, tuple(W_shard.shape))):
+        if (t.device != H.device or t.dtype != torch.float32
+                or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise VPCEError(f"{name} must be a contiguous fp32 {shape} tensor "
+                            "on H's device")
+    if (lse.device != H.device or lse.dtype != torch.float32
+            or lse.numel() != N or not lse.is_contiguous()):
+        raise VPCEError("lse must be a contiguous fp32 [N] tensor")
+    if (totals.device != H.device or totals.dtype != torch.float64
+            or totals.numel() != 2):
+        raise VPCEError("totals must be an fp64 [2] tensor on the device")
+    if dloss is not None and (dloss.device != H.device or dloss.numel() != 1
+                              or dloss.dtype != torch.float32):
+        raise VPCEError("dloss must be a one-element fp32 tensor")
+    ws = _shard_workspace(H, V, workspace)
+    with torch.cuda.device(H.device):
+        st = _load().vpce_shard_backward(
+            _ptr(H), _ptr(W_shard), _ptr(labels), _ptr(lse), _ptr(totals),
+            _ptr(dloss), N, d, V, v_begin, W_shard.shape[0], ignore_index,
+            _dtype_code(H.dtype), _ptr(dH), _ptr(dW_shard), _ptr(ws),
+            ws.numel(), _stream(H))
+    _check(st)

@@ -83,13 +83,15 @@ __device__ __forceinline__ int clamp_rows(int64_t remaining) {
 // ---------------------------------------------------------------------------
 struct FwdParams {
   const void* H;
-  const void* W;
+  const void* W;        // rows of vocabulary entries v_base .. v_base + V - 1
   const int64_t* labels;
   int64_t N, d, V, ignore_index;
-  int R, S, T;  // shards, splits per shard, token tiles
+  int R, S, T;  // shards of W's rows, splits per shard, token tiles
   float* part_m;  // [R*S][N], base-2 running max
   float* part_s;  // [R*S][N], running sum of 2^(y - m)
   float* tgt;     // [N] target logit (natural units)
+  int64_t v_base;  // vocabulary index of W's first row
+  int64_t V_lab;   // labels outside [0, V_lab) (and not ignored) are invalid
 };
 
 template <typename T>
@@ -105,7 +107,7 @@ void fwd_lse_kernel(FwdParams a) {
   grouped_tile(idx, a.T, a.R * a.S, kGroupFwd, it, g);
   const int r = g / a.S, j = g % a.S;
   const Shards sh{a.V, a.R};
-  const int64_t v0 = sh.begin(r), vw = sh.width(r);
+  const int64_t v0 = a.v_base + sh.begin(r), vw = sh.width(r);
   const int64_t vend = v0 + vw;
   const int Q = (int)((vw + kTile - 1) / kTile);
   const int q0 = (int)((int64_t)Q * j / a.S), q1 = (int)((int64_t)Q * (j + 1) / a.S);
@@ -114,7 +116,7 @@ void fwd_lse_kernel(FwdParams a) {
   const int64_t tok0 = (int64_t)it * kTile;
   if (tid < kTile) {
     const int64_t tok = tok0 + tid;
-    lab_s[tid] = tok < a.N ? label_code(a.labels[tok], a.ignore_index, a.V)
+    lab_s[tid] = tok < a.N ? label_code(a.labels[tok], a.ignore_index, a.V_lab)
                            : kLabIgnored;
   }
   const int lane = tid & 63, wave = tid >> 6;
@@ -132,7 +134,7 @@ void fwd_lse_kernel(FwdParams a) {
 
   for (int q = q0; q < q1; ++q) {
     const int64_t col0 = v0 + (int64_t)q * kTile;
-    const T* Wb = reinterpret_cast<const T*>(a.W) + col0 * a.d;
+    const T* Wb = reinterpret_cast<const T*>(a.W) + (col0 - a.v_base) * a.d;
     tile_mainloop<T>(acc, Hb, a.d, a_rows, Wb, a.d, clamp_rows(vend - col0),
                      a.d, smem);
     // columns of this lane: lc + 32*jj, jj = 0..3 (global vocabulary index;
@@ -283,9 +285,13 @@ __global__ __launch_bounds__(256) void merge_kernel(
   }
 }
 
+// Mean of the token losses from the per-block sums. With totals (fp64
+// [sum of token losses, count]) the sums are added to it first and loss is
+// the mean over everything accumulated there so far (loss may then be NULL).
 __global__ __launch_bounds__(256) void loss_kernel(const double* bsum,
                                                    const int* bcnt, int nb,
-                                                   float* loss) {
+                                                   float* loss,
+                                                   double* totals) {
   __shared__ double ssum[256];
   __shared__ long long scnt[256];
   double s = 0.0;
@@ -304,8 +310,30 @@ __global__ __launch_bounds__(256) void loss_kernel(const double* bsum,
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0)
-    loss[0] = scnt[0] > 0 ? (float)(ssum[0] / (double)scnt[0]) : 0.f;
+  if (threadIdx.x == 0) {
+    double sum = ssum[0], cnt = (double)scnt[0];
+    if (totals) {
+      sum += totals[0];
+      cnt += totals[1];
+      totals[0] = sum;
+      totals[1] = cnt;
+    }
+    if (loss) loss[0] = cnt > 0.0 ? (float)(sum / cnt) : 0.f;
+  }
+}
+
+// Fold the G split partials of one shard, in split order, into each token's
+// running base-2 state (m, s).
+__global__ __launch_bounds__(256) void fold_state_kernel(
+    const float* part_m, const float* part_s, int64_t N, int G,
+    float* state_m, float* state_s) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  float m = state_m[i], s = state_s[i];
+  for (int g = 0; g < G; ++g)
+    ms_merge(m, s, part_m[(int64_t)g * N + i], part_s[(int64_t)g * N + i]);
+  state_m[i] = m;
+  state_s[i] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -330,6 +358,16 @@ __global__ __launch_bounds__(1024) void scale_kernel(const int64_t* labels,
   if (threadIdx.x == 0) {
     const float up = dloss ? dloss[0] : 1.f;
     scale[0] = sc[0] > 0 ? (float)((double)up / (double)sc[0]) : 0.f;
+  }
+}
+
+// scale = dloss / n, n the token count accumulated in totals[1]
+__global__ void scale_from_totals_kernel(const double* totals,
+                                         const float* dloss, float* scale) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const double n = totals[1];
+    const float up = dloss ? dloss[0] : 1.f;
+    scale[0] = n > 0.0 ? (float)((double)up / n) : 0.f;
   }
 }
 
@@ -694,7 +732,8 @@ int32_t run_forward(const Plan& p, const void* H, const void* W,
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0, st,
                        tgt, p.N, NAN);
     VPCE_LAUNCH_CHECK();
-    FwdParams fp{H, W, labels, p.N, p.d, p.V, ignore_index, p.R, p.S, p.T, pm, ps, tgt};
+    FwdParams fp{H, W, labels, p.N, p.d, p.V, ignore_index, p.R, p.S, p.T,
+                 pm, ps, tgt, 0, p.V};
     const unsigned grid = (unsigned)((int64_t)p.T * p.R * p.S);
     hipLaunchKernelGGL(fwd_lse_kernel<T>, dim3(grid), dim3(kThreads), 0, st, fp);
     VPCE_LAUNCH_CHECK();
@@ -702,8 +741,82 @@ int32_t run_forward(const Plan& p, const void* H, const void* W,
                        tgt, labels, p.N, p.R * p.S, ignore_index, lse, bsum, bcnt);
     VPCE_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsum, bcnt, p.nb, loss);
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsum, bcnt, p.nb,
+                     loss, static_cast<double*>(nullptr));
   VPCE_LAUNCH_CHECK();
+  return VPCE_OK;
+}
+
+// H^T [d][N_pad] into the workspace, zero in the padding columns.
+template <typename U>
+int32_t transpose_h(const Plan& p, const void* H, char* ws, hipStream_t st) {
+  if (p.N_pad > 0) {
+    dim3 g((unsigned)((p.N_pad + 63) / 64), (unsigned)((p.d + 63) / 64));
+    hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st,
+                       reinterpret_cast<const U*>(H), p.d, p.N, p.d,
+                       reinterpret_cast<U*>(ws + p.o_HT), p.N_pad, p.N_pad);
+    VPCE_LAUNCH_CHECK();
+  }
+  return VPCE_OK;
+}
+
+// Backward over the vocabulary entries [v_first, v_first + v_count), whose
+// rows of W start at Wspan and whose rows of dW start at dWspan, in chunks of
+// p.C columns: recompute G for the chunk, dW rows = G^T H, dH += G W_chunk.
+// The first chunk overwrites dH unless dH_acc; dW rows are overwritten unless
+// dW_acc. H^T must already be in the workspace and *scale on the device.
+template <typename T, typename U>
+int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
+                      int64_t v_first, int64_t v_count, int64_t V_lab,
+                      const int64_t* labels, const float* lse,
+                      const float* scale, int64_t ignore_index, float* dH,
+                      bool dH_acc, float* dWspan, bool dW_acc, char* ws,
+                      hipStream_t st) {
+  void* HT = ws + p.o_HT;
+  void* G = ws + p.o_G;
+  void* GT = ws + p.o_GT;
+  void* WT = ws + p.o_WT;
+  const int TD = (int)((p.d + kTile - 1) / kTile);
+  bool acc_h = dH_acc;
+  for (int64_t c0 = 0; c0 < v_count; c0 += p.C) {
+    const int64_t ceff = (v_count - c0) < p.C ? (v_count - c0) : p.C;
+    const int64_t cpad = (ceff + 63) / 64 * 64;
+    const int64_t cv0 = v_first + c0;
+    const U* Wc = reinterpret_cast<const U*>(Wspan) + c0 * p.d;
+    // W^T chunk [d][C_pad], zero in the padding columns
+    {
+      dim3 g((unsigned)((cpad + 63) / 64), (unsigned)((p.d + 63) / 64));
+      hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st, Wc, p.d, ceff,
+                         p.d, reinterpret_cast<U*>(WT), cpad, cpad);
+      VPCE_LAUNCH_CHECK();
+    }
+    const int CT = (int)((cpad + kTile - 1) / kTile);
+    if (p.N > 0) {
+      GParams gp{H, Wc, labels, lse, scale, p.N, p.N_pad, p.d, V_lab,
+                 ignore_index, cv0, ceff, cpad, p.T, CT, G, GT};
+      hipLaunchKernelGGL(recompute_g_kernel<T>, dim3((unsigned)(p.T * CT)),
+                         dim3(kThreads), 0, st, gp);
+      VPCE_LAUNCH_CHECK();
+    }
+    // dW rows of the chunk = G^T H : A = G^T [C_pad x N_pad], B = H^T
+    {
+      const int TM = (int)((ceff + kTile - 1) / kTile);
+      ProdParams pp{GT, p.N_pad, ceff, HT, p.N_pad, p.d, p.N_pad,
+                    dWspan + c0 * p.d, p.d, TM, TD, dW_acc ? 1 : 0};
+      hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(TM * TD)), dim3(kThreads), 0,
+                         st, pp);
+      VPCE_LAUNCH_CHECK();
+    }
+    // dH (+)= G W_chunk : A = G [N x C_pad], B = W^T chunk [d x C_pad]
+    if (p.N > 0) {
+      ProdParams pp{G, cpad, p.N, WT, cpad, p.d, cpad, dH, p.d, p.T, TD,
+                    acc_h ? 1 : 0};
+      hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(p.T * TD)), dim3(kThreads), 0,
+                         st, pp);
+      VPCE_LAUNCH_CHECK();
+    }
+    acc_h = true;
+  }
   return VPCE_OK;
 }
 
@@ -713,69 +826,42 @@ int32_t run_backward(const Plan& p, const void* H, const void* W,
                      const float* dloss, int64_t ignore_index, float* dH,
                      float* dW, char* ws, hipStream_t st) {
   float* scale = reinterpret_cast<float*>(ws + p.o_scale);
-  void* HT = ws + p.o_HT;
-  void* G = ws + p.o_G;
-  void* GT = ws + p.o_GT;
-  void* WT = ws + p.o_WT;
   hipLaunchKernelGGL(scale_kernel, dim3(1), dim3(1024), 0, st, labels, p.N,
                      ignore_index, dloss, scale);
   VPCE_LAUNCH_CHECK();
-  if (p.N_pad > 0) {
-    // H^T [d][N_pad], zero in the padding columns
-    dim3 g((unsigned)((p.N_pad + 63) / 64), (unsigned)((p.d + 63) / 64));
-    hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st,
-                       reinterpret_cast<const U*>(H), p.d, p.N, p.d,
-                       reinterpret_cast<U*>(HT), p.N_pad, p.N_pad);
-    VPCE_LAUNCH_CHECK();
-  }
+  int32_t rc = transpose_h<U>(p, H, ws, st);
+  if (rc != VPCE_OK) return rc;
   const Shards sh{p.V, p.R};
-  const int TD = (int)((p.d + kTile - 1) / kTile);
-  bool first = true;
   for (int r = 0; r < p.R; ++r) {
     const int64_t v0 = sh.begin(r), vw = sh.width(r);
-    for (int64_t c0 = 0; c0 < vw; c0 += p.C) {
-      const int64_t ceff = (vw - c0) < p.C ? (vw - c0) : p.C;
-      const int64_t cpad = (ceff + 63) / 64 * 64;
-      const int64_t cv0 = v0 + c0;
-      const U* Wc = reinterpret_cast<const U*>(W) + cv0 * p.d;
-      // W^T chunk [d][C_pad], zero in the padding columns
-      {
-        dim3 g((unsigned)((cpad + 63) / 64), (unsigned)((p.d + 63) / 64));
-        hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st, Wc, p.d, ceff,
-                           p.d, reinterpret_cast<U*>(WT), cpad, cpad);
-        VPCE_LAUNCH_CHECK();
-      }
-      const int CT = (int)((cpad + kTile - 1) / kTile);
-      if (p.N > 0) {
-        GParams gp{H, Wc, labels, lse, scale, p.N, p.N_pad, p.d, p.V,
-                   ignore_index, cv0, ceff, cpad, p.T, CT, G, GT};
-        hipLaunchKernelGGL(recompute_g_kernel<T>, dim3((unsigned)(p.T * CT)),
-                           dim3(kThreads), 0, st, gp);
-        VPCE_LAUNCH_CHECK();
-      }
-      // dW rows [cv0, cv0 + ceff) = G^T H : A = G^T [C_pad x N_pad], B = H^T
-      {
-        const int TM = (int)((ceff + kTile - 1) / kTile);
-        ProdParams pp{GT, p.N_pad, ceff, HT, p.N_pad, p.d, p.N_pad,
-                      dW + cv0 * p.d, p.d, TM, TD, 0};
-        hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(TM * TD)), dim3(kThreads), 0,
-                           st, pp);
-        VPCE_LAUNCH_CHECK();
-      }
-      // dH (+)= G W_chunk : A = G [N x C_pad], B = W^T chunk [d x C_pad]
-      if (p.N > 0) {
-        ProdParams pp{G, cpad, p.N, WT, cpad, p.d, cpad, dH, p.d, p.T, TD,
-                      first ? 0 : 1};
-        hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(p.T * TD)), dim3(kThreads), 0,
-                           st, pp);
-        VPCE_LAUNCH_CHECK();
-      }
-      first = false;
-    }
+    rc = backward_span<T, U>(p, H, reinterpret_cast<const U*>(W) + v0 * p.d,
+                             v0, vw, p.V, labels, lse, scale, ignore_index,
+                             dH, r > 0, dW + v0 * p.d, false, ws, st);
+    if (rc != VPCE_OK) return rc;
   }
   return VPCE_OK;
 }
 
+// One batch meets one vocabulary shard: fold the shard's logits into the
+// batch's running state [m | s | t] (3 x N floats).
+template <typename T>
+int32_t run_shard_fold(const Plan& p, const void* H, const void* Wshard,
+                       int64_t v_begin, int64_t V_lab, const int64_t* labels,
+                       int64_t ignore_index, float* state, char* ws,
+                       hipStream_t st) {
+  if (p.N == 0) return VPCE_OK;
+  float* pm = reinterpret_cast<float*>(ws + p.o_pm);
+  float* ps = reinterpret_cast<float*>(ws + p.o_ps);
+  FwdParams fp{H, Wshard, labels, p.N, p.d, p.V, ignore_index, 1, p.S, p.T,
+               pm, ps, state + 2 * p.N, v_begin, V_lab};
+  hipLaunchKernelGGL(fwd_lse_kernel<T>, dim3((unsigned)((int64_t)p.T * p.S)),
+                     dim3(kThreads), 0, st, fp);
+  VPCE_LAUNCH_CHECK();
+  hipLaunchKernelGGL(fold_state_kernel, dim3((unsigned)((p.N + 255) / 256)),
+                     dim3(256), 0, st, pm, ps, p.N, p.S, state, state + p.N);
+  VPCE_LAUNCH_CHECK();
+  return VPCE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -856,6 +942,138 @@ int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
                                           ignore_index, dH, dW, ws, st);
   return run_backward<float, uint32_t>(p, H, W, labels, lse, dloss,
                                        ignore_index, dH, dW, ws, st);
+}
+
+int32_t vpce_state_init(float* state, int64_t N, void* stream) {
+  if (N < 0 || N > kMaxTokens) return VPCE_ERR_SHAPE;
+  if (N == 0) return VPCE_OK;
+  if (!state) return VPCE_ERR_NULL;
+  if (!aligned(state, 4)) return VPCE_ERR_ALIGN;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const dim3 g((unsigned)((N + 255) / 256));
+  hipLaunchKernelGGL(fill_kernel, g, dim3(256), 0, st, state, N, -INFINITY);
+  VPCE_LAUNCH_CHECK();
+  hipLaunchKernelGGL(fill_kernel, g, dim3(256), 0, st, state + N, N, 0.f);
+  VPCE_LAUNCH_CHECK();
+  hipLaunchKernelGGL(fill_kernel, g, dim3(256), 0, st, state + 2 * N, N, NAN);
+  VPCE_LAUNCH_CHECK();
+  return VPCE_OK;
+}
+
+int32_t vpce_shard_fold(const void* H, const void* W_shard,
+                        const int64_t* labels, int64_t N, int64_t d, int64_t V,
+                        int64_t v_begin, int64_t v_count,
+                        int64_t ignore_index, int32_t dtype, float* state,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const int32_t s = check_shape(N, d, V, 1, dtype);
+  if (s != VPCE_OK) return s;
+  if (v_begin < 0 || v_count < 1 || v_begin > V - v_count)
+    return VPCE_ERR_SHAPE;
+  if (!W_shard || !workspace) return VPCE_ERR_NULL;
+  if (N > 0 && (!H || !labels || !state)) return VPCE_ERR_NULL;
+  if ((H && !aligned(H, 16)) || !aligned(W_shard, 16) ||
+      (labels && !aligned(labels, 8)) || (state && !aligned(state, 4)) ||
+      !aligned(workspace, kAlign))
+    return VPCE_ERR_ALIGN;
+  const Plan p = make_plan(N, d, v_count, 1, dtype);
+  if (workspace_bytes < p.fwd_bytes) return VPCE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == VPCE_BF16)
+    return run_shard_fold<__bf16>(p, H, W_shard, v_begin, V, labels,
+                                  ignore_index, state, ws, st);
+  return run_shard_fold<float>(p, H, W_shard, v_begin, V, labels,
+                               ignore_index, state, ws, st);
+}
+
+int32_t vpce_state_finish(const float* state, const int64_t* labels,
+                          int64_t N, int64_t ignore_index, float* lse,
+                          double* totals, float* loss, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (N < 0 || N > kMaxTokens) return VPCE_ERR_SHAPE;
+  if (!totals || !workspace) return VPCE_ERR_NULL;
+  if (N > 0 && (!state || !labels || !lse)) return VPCE_ERR_NULL;
+  if ((state && !aligned(state, 4)) || (labels && !aligned(labels, 8)) ||
+      (lse && !aligned(lse, 4)) || !aligned(totals, 8) ||
+      (loss && !aligned(loss, 4)) || !aligned(workspace, kAlign))
+    return VPCE_ERR_ALIGN;
+  const int nb = (int)((N + 255) / 256);
+  const size_t o_bcnt = up((size_t)(nb > 0 ? nb : 1) * 8);
+  if (workspace_bytes < o_bcnt + up((size_t)(nb > 0 ? nb : 1) * 4))
+    return VPCE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  double* bsum = reinterpret_cast<double*>(workspace);
+  int* bcnt = reinterpret_cast<int*>(reinterpret_cast<char*>(workspace) + o_bcnt);
+  if (N > 0) {
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nb), dim3(256), 0, st,
+                       state, state + N, state + 2 * N, labels, N, 1,
+                       ignore_index, lse, bsum, bcnt);
+    VPCE_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsum, bcnt, nb,
+                     loss, totals);
+  VPCE_LAUNCH_CHECK();
+  return VPCE_OK;
+}
+
+int32_t vpce_shard_backward(const void* H, const void* W_shard,
+                            const int64_t* labels, const float* lse,
+                            const double* totals, const float* dloss,
+                            int64_t N, int64_t d, int64_t V, int64_t v_begin,
+                            int64_t v_count, int64_t ignore_index,
+                            int32_t dtype, float* dH, float* dW_shard,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const int32_t s = check_shape(N, d, V, 1, dtype);
+  if (s != VPCE_OK) return s;
+  if (v_begin < 0 || v_count < 1 || v_begin > V - v_count)
+    return VPCE_ERR_SHAPE;
+  if (!W_shard || !dW_shard || !totals || !workspace) return VPCE_ERR_NULL;
+  if (N > 0 && (!H || !labels || !lse || !dH)) return VPCE_ERR_NULL;
+  if ((H && !aligned(H, 16)) || !aligned(W_shard, 16) ||
+      (labels && !aligned(labels, 8)) || (lse && !aligned(lse, 4)) ||
+      !aligned(totals, 8) || (dloss && !aligned(dloss, 4)) ||
+      (dH && !aligned(dH, 4)) || !aligned(dW_shard, 4) ||
+      !aligned(workspace, kAlign))
+    return VPCE_ERR_ALIGN;
+  const int64_t C =
+      widest_chunk(N, d, v_count, 1, dtype, workspace_bytes, false);
+  if (C == 0) return VPCE_ERR_WORKSPACE;
+  const Plan p = make_plan(N, d, v_count, 1, dtype, C);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* scale = reinterpret_cast<float*>(ws + p.o_scale);
+  hipLaunchKernelGGL(scale_from_totals_kernel, dim3(1), dim3(64), 0, st,
+                     totals, dloss, scale);
+  VPCE_LAUNCH_CHECK();
+  int32_t rc;
+  if (dtype == VPCE_BF16) {
+    rc = transpose_h<uint16_t>(p, H, ws, st);
+    if (rc != VPCE_OK) return rc;
+    return backward_span<__bf16, uint16_t>(p, H, W_shard, v_begin, v_count, V,
+                                           labels, lse, scale, ignore_index,
+                                           dH, true, dW_shard, true, ws, st);
+  }
+  rc = transpose_h<uint32_t>(p, H, ws, st);
+  if (rc != VPCE_OK) return rc;
+  return backward_span<float, uint32_t>(p, H, W_shard, v_begin, v_count, V,
+                                        labels, lse, scale, ignore_index, dH,
+                                        true, dW_shard, true, ws, st);
+}
+
+int32_t vpce_ring_mode(int64_t N, int64_t d, int64_t V, int32_t R,
+                       int32_t dtype, int32_t* mode, size_t* activation_bytes,
+                       size_t* weight_bytes) {
+  const int32_t s = check_shape(N, d, V, R, dtype);
+  if (s != VPCE_OK) return s;
+  if (!mode || !activation_bytes || !weight_bytes) return VPCE_ERR_NULL;
+  const size_t esz = dtype == VPCE_BF16 ? 2 : 4;
+  const int64_t widest = (V + R - 1) / R;
+  *activation_bytes = (size_t)N * d * esz;
+  *weight_bytes = (size_t)widest * d * esz;
+  *mode = widest < N ? VPCE_RING_MOVE_WEIGHTS : VPCE_RING_MOVE_ACTIVATIONS;
+  return VPCE_OK;
 }
 
 const char* vpce_status_string(int32_t status) {
