@@ -103,13 +103,13 @@ def cpu_baseline(inp, target_s=15.0):
         oracle.backward(Hs, Wf, ys)
         return time.perf_counter() - t0
 
-    # Grow the sample until it takes at least half the target: small
+    # Grow the sample until it takes at least 70% of the target: small
     # samples carry fixed costs (the W conversion, thread start-up) that
     # make a one-shot extrapolation from a tiny probe undershoot.
     n = 32
     t = run(n)
-    while t < 0.5 * target_s and n < w.N:
-        grow = min(8.0, target_s / max(t, 1e-3))
+    while t < 0.7 * target_s and n < w.N:
+        grow = min(8.0, 1.25 * target_s / max(t, 1e-3))
         n = min(w.N, max(n + 32, int(n * grow) // 32 * 32))
         t = run(n)
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
