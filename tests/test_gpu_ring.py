@@ -138,3 +138,42 @@ def test_move_weights_order_on_shard_calls_matches_forward(vp):
     assert float((lse - ref_lse).abs().max().item()) <= 1e-5
     assert abs(float(loss.item()) - float(ref_loss.item())) <= \
         1e-6 * abs(float(ref_loss.item()))
+
+
+def test_shard_calls_on_empty_and_all_ignored_batches(vp):
+    d, V, R = 64, 700, 2
+    say(f"case ring edge cases d={d} V={V} R={R}")
+    b = _bounds(V, R)
+    dev = torch.device("cuda")
+    g = torch.Generator(device="cuda").manual_seed(9)
+    W = (torch.randn((V, d), device=dev, generator=g) * 0.1).to(torch.bfloat16)
+    totals = torch.zeros(2, dtype=torch.float64, device=dev)
+    # an empty batch folds, finishes and back-propagates to nothing
+    H0 = torch.empty((0, d), dtype=torch.bfloat16, device=dev)
+    L0 = torch.empty(0, dtype=torch.int64, device=dev)
+    st0 = vp.state_init(0, dev)
+    for i in range(R):
+        vp.shard_fold(H0, W[b[i]:b[i + 1]], L0, V, b[i], st0)
+    lse0, loss0 = vp.state_finish(st0, L0, totals)
+    # a batch whose every label is ignored adds no token and no gradient
+    N = 300
+    H = torch.randn((N, d), device=dev, generator=g).to(torch.bfloat16)
+    L = torch.full((N,), -100, dtype=torch.int64, device=dev)
+    st = vp.state_init(N, dev)
+    for i in range(R):
+        vp.shard_fold(H, W[b[i]:b[i + 1]], L, V, b[i], st)
+    lse, loss = vp.state_finish(st, L, totals)
+    dH = torch.zeros((N, d), dtype=torch.float32, device=dev)
+    dW = [torch.zeros((b[i + 1] - b[i], d), dtype=torch.float32, device=dev)
+          for i in range(R)]
+    for i in range(R):
+        vp.shard_backward(H, W[b[i]:b[i + 1]], L, lse, totals, None, V, b[i],
+                          dH, dW[i])
+    ref_loss, ref_lse = vp.forward(H, W, L, R)
+    torch.cuda.synchronize()
+    assert lse0.numel() == 0 and float(loss0.item()) == 0.0
+    assert totals.tolist() == [0.0, 0.0]
+    assert float(loss.item()) == 0.0 and float(ref_loss.item()) == 0.0
+    assert float((lse - ref_lse).abs().max().item()) <= 1e-5
+    assert bool((dH == 0).all().item())
+    assert all(bool((x == 0).all().item()) for x in dW)
