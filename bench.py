@@ -85,6 +85,48 @@ def traffic_record(workload: str):
     return rec
 
 
+class ClockSampler:
+    """Samples the shader clock of every XCD with `amd-smi metric --clock`
+    (a child process) while the timed steps run; reports the median of the
+    per-sample XCD means, or None where the tool is missing or fails."""
+
+    def __init__(self):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import subprocess
+        while not self._stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "--clock", "--json"],
+                                   capture_output=True, text=True, timeout=10)
+                data = json.loads(r.stdout)
+                gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+                clk = [v["clk"]["value"] for k, v in gpu["clock"].items()
+                       if k.startswith("gfx_")]
+                if clk:
+                    self.samples.append(sum(clk) / len(clk))
+            except Exception:
+                return
+            self._stop.wait(0.2)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=15)
+
+    def median(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return float(xs[len(xs) // 2])
+
+
 def cpu_baseline(inp, target_s=15.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same
     workload: the first n tokens against the full vocabulary (forward and
@@ -225,16 +267,17 @@ def main():
     t_all1 = torch.cuda.Event(enable_timing=True)
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_all0.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        loss, lse = vp.forward(H, W, lab, w.R, workspace=ws)
-        ev[k][1].record(stream)
-        dH, dW = vp.backward(H, W, lab, lse, dloss, w.R, workspace=ws)
-        ev[k][2].record(stream)
-    t_all1.record(stream)
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        wall0 = time.perf_counter()
+        t_all0.record(stream)
+        for k in range(args.steps):
+            ev[k][0].record(stream)
+            loss, lse = vp.forward(H, W, lab, w.R, workspace=ws)
+            ev[k][1].record(stream)
+            dH, dW = vp.backward(H, W, lab, lse, dloss, w.R, workspace=ws)
+            ev[k][2].record(stream)
+        t_all1.record(stream)
+        torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
     total_ms = t_all0.elapsed_time(t_all1)
     fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
@@ -298,7 +341,11 @@ def main():
                      "achieved": fwd_tf, "peak": peak_tf, "unit": "TFLOP/s",
                      "frac": fwd_tf / peak_tf, "traffic": traffic,
                      "flops_per_launch": fwd_flops,
-                     "launch_ms": fwd_avg},
+                     "launch_ms": fwd_avg,
+                     # the published peak assumes a 2400 MHz shader clock;
+                     # this is the clock the chip held during the timed steps
+                     "sclk_mhz_timed": clock.median(),
+                     "sclk_samples": len(clock.samples)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
