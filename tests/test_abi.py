@@ -220,3 +220,47 @@ def test_shard_calls_reject_bad_arguments(lib):
                               ctypes.byref(act), ctypes.byref(wts)) == 2
     assert lib.vpce_ring_mode(4, 16, 10, 2, 0, None, ctypes.byref(act),
                               ctypes.byref(wts)) == 1
+
+
+def test_bench_traffic_record_goes_stale_with_the_device_code(tmp_path,
+                                                             monkeypatch):
+    """A stored counter reading is used only while the device code it was
+    taken on is the one built now."""
+    import json
+    import bench
+    built = bench.kernel_code_hash()
+    rec = {"kernel_code_hash": built, "hbm_bytes_per_launch": 123}
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "fwd_lse_kernel_traffic_w.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_code_hash", lambda: built)
+    assert bench.traffic_record("w")["hbm_bytes_per_launch"] == 123
+    rec["kernel_code_hash"] = "0" * 16
+    (prof / "fwd_lse_kernel_traffic_w.json").write_text(json.dumps(rec))
+    assert bench.traffic_record("w") is None
+    assert bench.traffic_record("missing") is None
+
+
+def test_bench_clock_sampler_without_the_tool(monkeypatch):
+    """Without amd-smi (or when it fails) the sampled clock is reported as
+    None instead of failing the benchmark."""
+    import subprocess
+    import bench
+
+    def boom(*a, **k):
+        raise FileNotFoundError("amd-smi")
+    monkeypatch.setattr(subprocess, "run", boom)
+    with bench.ClockSampler() as c:
+        pass
+    assert c.median() is None and c.samples == []
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
