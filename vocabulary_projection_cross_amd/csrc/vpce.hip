@@ -377,7 +377,9 @@ template <typename U>
 __global__ __launch_bounds__(256) void transpose_kernel(
     const U* __restrict__ src, int64_t ld_src, int64_t rows, int64_t cols,
     U* __restrict__ dst, int64_t ld_dst, int64_t dst_cols) {
-  __shared__ U t[64][65];
+  // row stride an odd number of 4-byte words (65 for fp32, 66 halves = 33
+  // words for bf16), so the 64 lanes reading down a column hit 64 banks
+  __shared__ U t[64][sizeof(U) == 2 ? 66 : 65];
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int k = ty; k < 64; k += 4) {
