@@ -11,7 +11,7 @@
 // within the wave's sub-tile.
 //
 // Operands stream through a ring of NST LDS stages of RB bytes of K per row
-// (64 B x 4 stages by default), copied global -> LDS by buffer loads that
+// (128 B x 2 stages by default), copied global -> LDS by buffer loads that
 // write LDS directly, NST - 1 stages ahead of the MFMAs. Within a row the
 // 16-byte chunk index is XOR-swizzled by row bits, so the MFMA fragment reads
 // (consecutive rows, same chunk) hit distinct banks whether the LDS serves 8
@@ -338,17 +338,18 @@ __device__ __forceinline__ void tile_mainloop_ring(
 }
 
 // Build-time shape of the engine (measured on the 1M-context slice: 4 x 2
-// waves with a 4-deep ring of 64-byte slabs is the fastest of the shapes
-// tried; 2 x 2 waves and a 2-deep ring of 128-byte slabs also work, and a
-// 3- or 5-deep ring times the same).
+// waves with a 2-deep ring of 128-byte slabs is the fastest of the shapes
+// tried, 4% ahead of a 4-deep ring of 64-byte slabs over a full step: whole
+// 128-byte lines per request, a barrier every four K-steps instead of two;
+// 2 x 2 waves also work, and 3-, 4- or 5-deep 64-byte rings time the same).
 #ifndef VPCE_WAVES_M
 #define VPCE_WAVES_M 4
 #endif
 #ifndef VPCE_RING_RB
-#define VPCE_RING_RB 64
+#define VPCE_RING_RB 128
 #endif
 #ifndef VPCE_RING_NST
-#define VPCE_RING_NST 4
+#define VPCE_RING_NST 2
 #endif
 
 // The configuration every GEMM phase uses.
