@@ -33,7 +33,7 @@
  *    enqueued. A failed kernel launch returns VPCE_ERR_HIP.
  *  - Functions are reentrant; the library keeps no state between calls.
  *    Concurrent calls must use distinct workspaces.
- *  - Requirements: 0 <= N <= 2000000, 1 <= d <= 2000000, V >= 1,
+ *  - Requirements: 0 <= N <= 2000000, 1 <= d <= 1000000, V >= 1,
  *    1 <= R <= V, V < 2^31, d a multiple of 8 (VPCE_BF16) or 4 (VPCE_F32),
  *    H and W 16-byte aligned,
  *    every other pointer 4-byte aligned (labels 8, workspace 256).

@@ -63,6 +63,11 @@ def test_workspace_rejects_bad_shapes(lib):
     assert lib.vpce_workspace_bytes(10, 16, 5, 1, 7) == 0     # dtype
     assert lib.vpce_workspace_bytes(10, 16, 1 << 31, 1, 0) == 0
     assert lib.vpce_workspace_bytes(0, 16, 5, 1, 0) > 0       # empty batch
+    # hidden size: 320 rows of an fp32 operand must stay below 2^31 bytes
+    assert lib.vpce_workspace_bytes(1, 1_000_000, 5, 1, 1) > 0
+    assert lib.vpce_workspace_bytes(1, 1_000_008, 5, 1, 0) == 0
+    assert lib.vpce_workspace_bytes(2_000_000, 16, 5, 1, 0) > 0
+    assert lib.vpce_workspace_bytes(2_000_001, 16, 5, 1, 0) == 0
 
 
 def _fwd(lib, H=8, W=16, lab=8, N=4, d=16, V=10, R=2, dt=0, loss=4, lse=4,

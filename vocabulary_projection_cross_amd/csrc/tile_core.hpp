@@ -1,11 +1,11 @@
 // tile_core.hpp -- the MFMA tile engine shared by every GEMM phase of the
 // blocked vocabulary-projection cross-entropy on gfx950 (CDNA4).
 //
-// A workgroup computes one 256 x 256 fp32 tile C = A . B^T where A [M x K]
-// and B [Nc x K] are both row-major with K contiguous ("NT" form). Its waves
-// split the tile as Layout<WM, WN> says (4 x 2 waves of 64 x 128 by default,
-// two waves per SIMD); each wave holds its sub-tile as R x C accumulators of
-// the 32x32 MFMA layout:
+// A workgroup computes one TM x TN fp32 tile C = A . B^T where A [M x K] and
+// B [Nc x K] are both row-major with K contiguous ("NT" form). Its waves split
+// the tile as Layout<TM, TN, WM, WN> says (4 x 2 waves, two per SIMD, of
+// 64 x 128 on a 256 x 256 tile or 64 x 160 on a 256 x 320 tile); each wave
+// holds its sub-tile as R x C accumulators of the 32x32 MFMA layout:
 //   element r (0..15) of accumulator (i, j) on lane l is
 //   row = i*32 + 8*(r/4) + 4*(l/32) + (r%4),  col = j*32 + (l%32)
 // within the wave's sub-tile.
@@ -28,57 +28,74 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kTile = 256;                          // BM = BN
-constexpr int kGemmLds = 128 * 1024;                // LDS of the operand ring
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one workgroup on gfx950
 
 // Elements of T per 16-byte chunk.
 template <typename T> struct Chunk;
 template <> struct Chunk<__bf16> { static constexpr int E = 8; };
 template <> struct Chunk<float> { static constexpr int E = 4; };
 
-// How the waves of a workgroup split the 256 x 256 tile: WM x WN waves, each
-// owning a (256/WM) x (256/WN) sub-tile held as R x C accumulators of the
-// 32x32 MFMA layout. Wave w sits at (w / WN, w % WN). With 8 waves two of
-// them share each SIMD, so one wave's MFMAs keep the matrix unit busy while
-// the other waits to issue a copy or an LDS read.
-template <int WM_, int WN_>
+// How the waves of a workgroup split a TM x TN tile: WM x WN waves, each
+// owning a (TM/WM) x (TN/WN) sub-tile held as R x C accumulators of the 32x32
+// MFMA layout. Wave w sits at (w / WN, w % WN). With 8 waves two of them share
+// each SIMD, so one wave's MFMAs keep the matrix unit busy while the other
+// waits to issue a copy or an LDS read.
+//
+// Per K-step a wave runs its R x C MFMAs in NG groups along its longer side
+// (column groups when C > R: group j pairs B fragment j with every A
+// fragment), and spreads the next step's fragment reads and, after the
+// barrier, the stage's copies over those groups. Many small groups issue the
+// copies in small bunches between MFMAs: on a 64 x 160 sub-tile five column
+// groups of two MFMAs take 7% less time than two row groups of five.
+template <int TM_, int TN_, int WM_, int WN_>
 struct Layout {
-  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kWaveRows = kTile / WM;
-  static constexpr int kWaveCols = kTile / WN;
+  static constexpr int kWaveRows = TM / WM;
+  static constexpr int kWaveCols = TN / WN;
   static constexpr int R = kWaveRows / 32;  // accumulator row blocks
   static constexpr int C = kWaveCols / 32;  // accumulator column blocks
+  static constexpr bool kColGroups = C > R;
+  static constexpr int NG = kColGroups ? C : R;  // MFMA groups per K-step
+  static_assert(kWaveRows * WM == TM && kWaveCols * WN == TN &&
+                    kWaveRows % 32 == 0 && kWaveCols % 32 == 0,
+                "whole 32 x 32 blocks per wave");
 };
 
 // Shape of the operand ring: RB bytes of K per row per stage, NST stages.
-// A stage holds both 256-row operand tiles; copies run NST - 1 stages ahead.
+// A stage holds the TM-row A tile and the TN-row B tile; copies run NST - 1
+// stages ahead.
 //   RB = 64:  chunk slot = chunk ^ ((row >> 1) ^ (row >> 2)) & 3
 //   RB = 128: chunk slot = chunk ^ (row & 7) ^ ((row >> 3) & 1)
 // Either way, 8 consecutive rows read at one chunk fill a 128-byte bank
 // window exactly once and 16 consecutive rows fill a 256-byte window once.
-template <int RB, int NST, int WAVES>
+template <int RB, int NST, int TM, int TN, int WAVES>
 struct Ring {
   static_assert(RB == 64 || RB == 128, "row bytes per stage");
   static constexpr int kChunks = RB / 16;              // chunks per row
   static constexpr int kSteps = RB / 32;               // MFMA K-steps
   static constexpr int kBlockRows = 1024 / RB;         // rows per 1 KiB copy
-  static constexpr int kBlocks = kTile / kBlockRows / WAVES;  // per wave/op
-  static constexpr int kOperandBytes = kTile * RB;
-  static constexpr int kStageBytes = 2 * kOperandBytes;
-  static constexpr int kCopies = 2 * kBlocks;          // per wave per stage
-  static_assert(kBlocks >= 1, "every wave copies at least one block");
-  static_assert(RB == 64 || kBlocks % 2 == 0, "block parity fixes the swizzle");
-  static_assert(NST * kStageBytes <= kGemmLds, "ring exceeds LDS budget");
+  static constexpr int kBlocksA = TM / kBlockRows / WAVES;  // per wave
+  static constexpr int kBlocksB = TN / kBlockRows / WAVES;
+  static constexpr int kOperandBytesA = TM * RB;
+  static constexpr int kStageBytes = (TM + TN) * RB;
+  static constexpr int kBytes = NST * kStageBytes;
+  static constexpr int kCopies = kBlocksA + kBlocksB;  // per wave per stage
+  static_assert(kBlocksA * kBlockRows * WAVES == TM &&
+                    kBlocksB * kBlockRows * WAVES == TN && kBlocksA >= 1 &&
+                    kBlocksB >= 1,
+                "every wave copies whole blocks of both operands");
+  static_assert(kBytes <= kLdsBytes, "ring exceeds the LDS");
   __device__ static constexpr int swz(int row) {
     return RB == 64 ? ((row >> 1) ^ (row >> 2)) & 3
                     : (row & 7) ^ ((row >> 3) & 1);
   }
 };
 
-// One K-step of one accumulator row block (C accumulators sharing the A
-// fragment): each lane supplies 16 bytes of A and 16 bytes of B per block.
+// One K-step of MFMA group q (see Layout): row group q updates accumulators
+// (q, 0..C-1), column group q updates (0..R-1, q). Each lane supplies 16
+// bytes of A and 16 bytes of B per 32 x 32 block.
 //   bf16: one v_mfma_f32_32x32x16_bf16 per accumulator (lane half h carries
 //         k = 8h..8h+7 of the step's 16).
 //   fp32: four v_mfma_f32_32x32x2_f32 per accumulator; instruction e pairs
@@ -86,29 +103,35 @@ struct Ring {
 //         B that is the same on both operands gives the same sum.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int C>
-__device__ __forceinline__ void mma_row(f32x16_t (&acc)[C], u32x4_t a,
-                                        const u32x4_t (&b)[C],
-                                        const __bf16*) {
+template <typename L>
+__device__ __forceinline__ void mma_group(f32x16_t (&acc)[L::R][L::C],
+                                          const u32x4_t (&a)[L::R],
+                                          const u32x4_t (&b)[L::C], int q,
+                                          const __bf16*) {
+  constexpr int GS = L::kColGroups ? L::R : L::C;
 #pragma unroll
-  for (int j = 0; j < C; ++j)
-    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[j]),
-        acc[j], 0, 0, 0);
+  for (int g = 0; g < GS; ++g) {
+    const int i = L::kColGroups ? g : q, j = L::kColGroups ? q : g;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, b[j]),
+        acc[i][j], 0, 0, 0);
+  }
 }
-template <int C>
-__device__ __forceinline__ void mma_row(f32x16_t (&acc)[C], u32x4_t a,
-                                        const u32x4_t (&b)[C], const float*) {
-  const f32x4_t af = __builtin_bit_cast(f32x4_t, a);
-  f32x4_t bf[C];
-#pragma unroll
-  for (int j = 0; j < C; ++j) bf[j] = __builtin_bit_cast(f32x4_t, b[j]);
+template <typename L>
+__device__ __forceinline__ void mma_group(f32x16_t (&acc)[L::R][L::C],
+                                          const u32x4_t (&a)[L::R],
+                                          const u32x4_t (&b)[L::C], int q,
+                                          const float*) {
+  constexpr int GS = L::kColGroups ? L::R : L::C;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int j = 0; j < C; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[j][e], acc[j],
-                                                    0, 0, 0);
+    for (int g = 0; g < GS; ++g) {
+      const int i = L::kColGroups ? g : q, j = L::kColGroups ? q : g;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+          __builtin_bit_cast(f32x4_t, a[i])[e],
+          __builtin_bit_cast(f32x4_t, b[j])[e], acc[i][j], 0, 0, 0);
+    }
 }
 
 typedef __attribute__((address_space(3))) char lds_char_t;
@@ -145,9 +168,8 @@ __device__ __forceinline__ void copy16_to_lds(uint32_t lds_addr,
 }
 
 // A byte offset that every buffer resource here rejects (loads read zero).
-// Resources span less than 2^31 bytes and a block offset (fewer than 32
-// blocks of at most 16 rows, rows below 2^23 bytes) added to it stays below
-// 2^32, so it stays rejected.
+// Resources span less than 2^31 bytes and a block offset (fewer than 64 rows
+// of at most 2^22 bytes) added to it stays below 2^32, so it stays rejected.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
@@ -156,34 +178,34 @@ constexpr int waitcnt_vm_lgkm(int vm, int lgkm) {
   return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
 }
 
-// acc = A[0:256, 0:K] . B[0:256, 0:K]^T for the workgroup's tile; this wave's
+// acc = A[0:TM, 0:K] . B[0:TN, 0:K]^T for the workgroup's tile; this wave's
 // sub-tile lands in acc (layout L). A, B point at the tile's first row;
-// a_rows / b_rows are the valid rows (clamped by the caller to [0, 256]);
-// 256 * ld * sizeof(T) must stay below 2^31 bytes and K must be a multiple of
-// 16 bytes' worth of T (checked on the host). smem must hold kGemmLds bytes.
-// Ends with every copy landed and a workgroup barrier, so smem may be reused
-// right after.
+// a_rows / b_rows are the valid rows (clamped by the caller to [0, TM] and
+// [0, TN]); TM * ld * sizeof(T) and TN * ld * sizeof(T) must stay below 2^31
+// bytes and K must be a multiple of 16 bytes' worth of T (checked on the
+// host). smem must hold the ring's kBytes. Ends with every copy landed and a
+// workgroup barrier, so smem may be reused right after.
 //
 // Global memory is copied straight into LDS by the buffer-load-to-LDS path
-// (no register staging): each wave copies kBlocks 1 KiB blocks of each
-// operand per stage; lane l of a block copies row l / kChunks into slot
+// (no register staging): per stage each wave copies kBlocksA 1 KiB blocks of
+// A and kBlocksB of B; lane l of a block copies row l / kChunks into slot
 // l % kChunks of that row, which holds the global chunk slot ^ swz(row).
-// Per stage kt (ring buffer kt % NST), each of its S K-steps runs R row
-// groups of C MFMAs, with the next step's fragments read at the step's
-// start; the last step starts with the workgroup barrier, after which the
-// wave reads stage kt + 1's first fragments and issues its copies of stage
-// kt + NST into the buffer stage kt leaves (see the loop for why that order
-// is safe).
+// Per stage kt (ring buffer kt % NST), each of its S K-steps runs the NG MFMA
+// groups, with the next step's fragments read at the step's start; the last
+// step starts with the workgroup barrier, after which the wave reads stage
+// kt + 1's first fragments and issues its copies of stage kt + NST into the
+// buffer stage kt leaves (see the loop for why that order is safe).
 template <typename T, typename L, int RB, int NST>
 __device__ __forceinline__ void tile_mainloop_ring(
     f32x16_t (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
     int a_rows, const T* __restrict__ B, int64_t ldb, int b_rows, int64_t K,
     char* smem) {
-  using P = Ring<RB, NST, L::kWaves>;
-  constexpr int R = L::R, C = L::C;
+  using P = Ring<RB, NST, L::TM, L::TN, L::kWaves>;
+  constexpr int R = L::R, C = L::C, NG = L::NG;
   constexpr int E = Chunk<T>::E;           // elements per 16-byte chunk
   constexpr int BK = RB / (int)sizeof(T);  // elements of K per stage
   constexpr int S = P::kSteps;
+  constexpr int KA = P::kBlocksA, KB = P::kBlocksB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int swave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
   const int wm = wave / L::WN, wn = wave % L::WN;
@@ -201,74 +223,92 @@ __device__ __forceinline__ void tile_mainloop_ring(
   const i32x4_t rsb = tile_rsrc_dw<T>(B, ldb, b_rows);
   const uint32_t lds = (uint32_t)(uintptr_t)(lds_char_t*)smem;
 
-  // copy side: blocks kBlocks*w .. kBlocks*w + kBlocks-1 of both operands.
-  // The swizzle of a row depends on its bits 0..3; block starts are
-  // multiples of kBlockRows, so the lane's chunk depends on the block only
-  // through bit 3 of its first row (RB = 128: blocks of 8 rows, an even
-  // number per wave, so that bit is the parity of u).
+  // copy side: blocks KA*w .. KA*w + KA-1 of A and KB*w .. of B. The swizzle
+  // of a row depends on its bits 0..3; block starts are multiples of
+  // kBlockRows, so the lane's chunk depends on the block only through bit 3
+  // of its first row (RB = 128: blocks of 8 rows, bit 3 = parity of the
+  // block's index in the tile, KX*w + u). Per operand, cx[e] is the lane's
+  // chunk for the wave's blocks u with u % 2 == e.
   const int crow = lane / P::kChunks;
   const int slot = lane % P::kChunks;
   const int ch0 = slot ^ P::swz(crow);
   const int ch1 = slot ^ P::swz(crow + 8);
+  const int par_a = RB == 128 ? (swave * KA) & 1 : 0;
+  const int par_b = RB == 128 ? (swave * KB) & 1 : 0;
+  const int ca[2] = {par_a ? ch1 : ch0, par_a ? ch0 : ch1};
+  const int cb[2] = {par_b ? ch1 : ch0, par_b ? ch0 : ch1};
   const uint32_t pa = (uint32_t)(lda * (int64_t)sizeof(T));
   const uint32_t pb = (uint32_t)(ldb * (int64_t)sizeof(T));
-  const uint32_t row0 = (uint32_t)(swave * P::kBlocks * P::kBlockRows + crow);
-  const uint32_t cdst = lds + (uint32_t)(swave * P::kBlocks * 1024);
-  // stages whose chunk (for even/odd blocks) lies inside K:
-  // s * BK + ch * E < K  <=>  s < klim
+  const uint32_t rowa = (uint32_t)(swave * KA * P::kBlockRows + crow);
+  const uint32_t rowb = (uint32_t)(swave * KB * P::kBlockRows + crow);
+  const uint32_t dsta = lds + (uint32_t)(swave * KA * 1024);
+  const uint32_t dstb = lds + (uint32_t)(P::kOperandBytesA + swave * KB * 1024);
+  // stages whose chunk lies inside K: s * BK + ch * E < K  <=>  s < klim
   const int Ki = (int)K;  // K < 2^31 (checked on the host)
-  const int klim0 = Ki > ch0 * E ? (Ki - ch0 * E + BK - 1) / BK : 0;
-  const int klim1 = Ki > ch1 * E ? (Ki - ch1 * E + BK - 1) / BK : 0;
-  const uint32_t ra0 = row0 * pa + (uint32_t)(ch0 * 16);
-  const uint32_t ra1 = row0 * pa + (uint32_t)(ch1 * 16);
-  const uint32_t rb0 = row0 * pb + (uint32_t)(ch0 * 16);
-  const uint32_t rb1 = row0 * pb + (uint32_t)(ch1 * 16);
+  auto klim = [&](int ch) {
+    return Ki > ch * E ? (Ki - ch * E + BK - 1) / BK : 0;
+  };
+  const int kla[2] = {klim(ca[0]), klim(ca[1])};
+  const int klb[2] = {klim(cb[0]), klim(cb[1])};
+  const uint32_t ra[2] = {rowa * pa + (uint32_t)(ca[0] * 16),
+                          rowa * pa + (uint32_t)(ca[1] * 16)};
+  const uint32_t rb[2] = {rowb * pb + (uint32_t)(cb[0] * 16),
+                          rowb * pb + (uint32_t)(cb[1] * 16)};
+  constexpr int NE = RB == 128 ? 2 : 1;  // chunk parities in use
   uint32_t va[2], vb[2];
-  // lane offsets of stage s for even/odd blocks (past K -> out of range)
+  // lane offsets of stage s (past K -> out of range)
   auto stage_offsets = [&](int s) {
     const uint32_t ko = (uint32_t)s * (uint32_t)RB;
-    va[0] = s < klim0 ? ra0 + ko : kOutOfRange;
-    vb[0] = s < klim0 ? rb0 + ko : kOutOfRange;
-    if (RB == 128) {
-      va[1] = s < klim1 ? ra1 + ko : kOutOfRange;
-      vb[1] = s < klim1 ? rb1 + ko : kOutOfRange;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      va[e] = s < kla[e] ? ra[e] + ko : kOutOfRange;
+      vb[e] = s < klb[e] ? rb[e] + ko : kOutOfRange;
     }
   };
-  // copy c of a stage: even c -> A block c/2, odd c -> B block c/2
+  // copy c of a stage: A and B blocks alternate while both last, then the
+  // rest of the larger operand
+  constexpr int MinAB = KA < KB ? KA : KB;
   auto copy_one = [&](int s, int c) {
-    const int u = c >> 1;
-    const uint32_t dst =
-        cdst + (uint32_t)((s % NST) * P::kStageBytes + u * 1024);
-    const int e = (RB == 128) ? (u & 1) : 0;
+    const bool is_a = c < 2 * MinAB ? (c & 1) == 0 : KA > KB;
+    const int u = c < 2 * MinAB ? c >> 1 : MinAB + (c - 2 * MinAB);
+    const uint32_t boff = (uint32_t)((s % NST) * P::kStageBytes + u * 1024);
     const uint32_t rows = (uint32_t)(u * P::kBlockRows);
-    if ((c & 1) == 0)
-      copy16_to_lds(dst, va[e] + rows * pa, rsa);
+    const int e = NE == 2 ? (u & 1) : 0;
+    if (is_a)
+      copy16_to_lds(dsta + boff, va[e] + rows * pa, rsa);
     else
-      copy16_to_lds(dst + P::kOperandBytes, vb[e] + rows * pb, rsb);
+      copy16_to_lds(dstb + boff, vb[e] + rows * pb, rsb);
   };
 
   // fragment side: lane (p, h) reads row (base + 32*i + p) at chunk 2s + h;
   // rows differ from p by multiples of 32, so the swizzle is swz(p).
   const int g = P::swz(p);
   const int fa = (wm * L::kWaveRows + p) * RB;
-  const int fb = P::kOperandBytes + (wn * L::kWaveCols + p) * RB;
+  const int fb = P::kOperandBytesA + (wn * L::kWaveCols + p) * RB;
   int fo[S];
 #pragma unroll
   for (int st = 0; st < S; ++st) fo[st] = ((2 * st + h) ^ g) << 4;
   u32x4_t af[2][R], bfr[2][C];
-  // read number n of a step's R + C fragment reads: A0, B0..B(C-1),
-  // A1..A(R-1)
+  // read number n of a step's R + C fragment reads, in the order the groups
+  // need them: row groups A0, B0..B(C-1), A1..A(R-1); column groups B0,
+  // A0..A(R-1), B1..B(C-1)
   constexpr int kReads = R + C;
   auto read_one = [&](int stage_off, int st, int buf, int n) {
-    if (n == 0 || n > C) {
-      const int i = n == 0 ? 0 : n - C;
-      af[buf][i] = *reinterpret_cast<const u32x4_t*>(
-          smem + stage_off + fa + fo[st] + i * 32 * RB);
+    bool is_a;
+    int x;
+    if (!L::kColGroups) {
+      is_a = n == 0 || n > C;
+      x = n == 0 ? 0 : (n > C ? n - C : n - 1);
     } else {
-      const int j = n - 1;
-      bfr[buf][j] = *reinterpret_cast<const u32x4_t*>(
-          smem + stage_off + fb + fo[st] + j * 32 * RB);
+      is_a = n >= 1 && n <= R;
+      x = n == 0 ? 0 : (n <= R ? n - 1 : n - R);
     }
+    if (is_a)
+      af[buf][x] = *reinterpret_cast<const u32x4_t*>(
+          smem + stage_off + fa + fo[st] + x * 32 * RB);
+    else
+      bfr[buf][x] = *reinterpret_cast<const u32x4_t*>(
+          smem + stage_off + fb + fo[st] + x * 32 * RB);
   };
   // reads [n0, n1) of a step
   auto reads = [&](int stage_off, int st, int buf, int n0, int n1) {
@@ -289,8 +329,8 @@ __device__ __forceinline__ void tile_mainloop_ring(
   reads(0, 0, 0, 0, kReads);
   const T* tag = nullptr;
 
-  // Each step's fragment reads are spread over the previous step's row
-  // groups (A0 and the B fragments first). The last step of stage kt opens
+  // Each step's fragment reads are spread over the previous step's groups
+  // (the first group's fragments first). The last step of stage kt opens
   // with the barrier, which waits until this wave's copies of stage kt + 1
   // have landed and its own LDS reads have completed: after it every wave
   // holds stage kt's fragments in registers, so buffer kt % NST is free and
@@ -302,7 +342,7 @@ __device__ __forceinline__ void tile_mainloop_ring(
   auto copies_at = [&](int s, int grp) {
 #pragma unroll
     for (int c = 0; c < P::kCopies; ++c)
-      if (c * R / P::kCopies == grp) copy_one(s, c);
+      if (c * NG / P::kCopies == grp) copy_one(s, c);
   };
 
   for (int kt = 0; kt < KT; ++kt) {
@@ -311,10 +351,10 @@ __device__ __forceinline__ void tile_mainloop_ring(
 #pragma unroll
     for (int st = 0; st < S - 1; ++st) {
 #pragma unroll
-      for (int q = 0; q < R; ++q) {
-        reads(cur, st + 1, (st + 1) & 1, q * kReads / R,
-              (q + 1) * kReads / R);
-        mma_row<C>(acc[q], af[st & 1][q], bfr[st & 1], tag);
+      for (int q = 0; q < NG; ++q) {
+        reads(cur, st + 1, (st + 1) & 1, q * kReads / NG,
+              (q + 1) * kReads / NG);
+        mma_group<L>(acc, af[st & 1], bfr[st & 1], q, tag);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -324,10 +364,10 @@ __device__ __forceinline__ void tile_mainloop_ring(
     __builtin_amdgcn_sched_barrier(0);
     stage_offsets(kt + NST);
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      reads(nxt, 0, 0, q * kReads / R, (q + 1) * kReads / R);
+    for (int q = 0; q < NG; ++q) {
+      reads(nxt, 0, 0, q * kReads / NG, (q + 1) * kReads / NG);
       copies_at(kt + NST, q);
-      mma_row<C>(acc[q], af[LB][q], bfr[LB], tag);
+      mma_group<L>(acc, af[LB], bfr[LB], q, tag);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -337,11 +377,12 @@ __device__ __forceinline__ void tile_mainloop_ring(
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Build-time shape of the engine (measured on the 1M-context slice: 4 x 2
-// waves with a 2-deep ring of 128-byte slabs is the fastest of the shapes
-// tried, 4% ahead of a 4-deep ring of 64-byte slabs over a full step: whole
-// 128-byte lines per request, a barrier every four K-steps instead of two;
-// 2 x 2 waves also work, and 3-, 4- or 5-deep 64-byte rings time the same).
+// Build-time shape of the engine. Measured on the 1M-context slice: a 2-deep
+// ring of 128-byte slabs is 4% ahead of a 4-deep ring of 64-byte slabs over a
+// full step (whole 128-byte lines per request, a barrier every four K-steps
+// instead of two), and 4 x 2 waves ahead of 2 x 2. 64-byte slabs copy 16-row
+// blocks, which a 320-row operand does not split into over 8 waves, so they
+// build only with VPCE_WIDE_COLS=256.
 #ifndef VPCE_WAVES_M
 #define VPCE_WAVES_M 4
 #endif
@@ -351,18 +392,25 @@ __device__ __forceinline__ void tile_mainloop_ring(
 #ifndef VPCE_RING_NST
 #define VPCE_RING_NST 2
 #endif
+#ifndef VPCE_WIDE_COLS
+#define VPCE_WIDE_COLS 320
+#endif
 
-// The configuration every GEMM phase uses.
-using TileLayout = Layout<VPCE_WAVES_M, 2>;
-constexpr int kThreads = TileLayout::kThreads;
+// The two configurations: 256 x 256 tiles for the dW and dH products (whose
+// output dimensions are multiples of 256 in the usual shapes), 256 x 320 tiles
+// (vocabulary on the 320 side) for the forward and the logit recompute.
+using TileLayout = Layout<256, 256, VPCE_WAVES_M, 2>;
+using WideLayout = Layout<256, VPCE_WIDE_COLS, 4, 2>;
+template <typename L>
+using RingOf = Ring<VPCE_RING_RB, VPCE_RING_NST, L::TM, L::TN, L::kWaves>;
 
-// smem must hold kGemmLds bytes.
-template <typename T>
+// smem must hold RingOf<L>::kBytes.
+template <typename T, typename L>
 __device__ __forceinline__ void tile_mainloop(
-    f32x16_t (&acc)[TileLayout::R][TileLayout::C], const T* __restrict__ A,
-    int64_t lda, int a_rows, const T* __restrict__ B, int64_t ldb,
-    int b_rows, int64_t K, char* smem) {
-  tile_mainloop_ring<T, TileLayout, VPCE_RING_RB, VPCE_RING_NST>(
+    f32x16_t (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
+    int a_rows, const T* __restrict__ B, int64_t ldb, int b_rows, int64_t K,
+    char* smem) {
+  tile_mainloop_ring<T, L, VPCE_RING_RB, VPCE_RING_NST>(
       acc, A, lda, a_rows, B, ldb, b_rows, K, smem);
 }
 

@@ -4,7 +4,7 @@
 //
 // Forward: the R vocabulary shards are the rounds of the ring. A workgroup
 // owns one 256-token tile, one shard and one contiguous split of that shard's
-// 256-column vocabulary tiles. For each vocabulary tile it forms the logit
+// 320-column vocabulary tiles. For each vocabulary tile it forms the logit
 // tile with MFMA (never leaving registers), folds it into a per-token running
 // (max, sum-exp) state with the online-softmax update, and picks up the target
 // logit if the tile owns the label. At the end of the split the state is
@@ -42,6 +42,7 @@ constexpr int kChunkCols = 16384;
 constexpr int kChunkStep = 256;
 constexpr int kMaxSplits = 16;
 constexpr int64_t kMaxTokens = 2000000;
+constexpr int64_t kMaxHidden = 1000000;  // 320 rows of d fp32 stay below 2^31 B
 // Grouped raster (consecutive workgroups of an XCD share operand rows): how
 // many token / output-row tiles sweep the column tiles together. Measured on
 // the 1M-context slice: 2 suits the forward, 8 the backward products.
@@ -50,9 +51,14 @@ constexpr int kGroupBwd = 8;  // the backward's dW and dH products
 constexpr int kGroupRec = 4;  // the backward's logit recompute
 constexpr int kLabIgnored = -2;   // label slot codes in LDS
 constexpr int kLabInvalid = -1;
-using TL = TileLayout;
-constexpr int kWavesPerSimd = TL::kWaves / 4;
-static_assert(TL::WN == 2, "forward row merge pairs two waves per row");
+using TL = TileLayout;  // dW and dH products
+using FL = WideLayout;  // forward and logit recompute: 256 tokens x FL::TN
+constexpr int kTile = 256;  // token tile of every kernel; product tile side
+static_assert(FL::TM == kTile && TL::TM == kTile && TL::TN == kTile,
+              "token tiles and product tiles are 256 rows");
+static_assert(FL::WN == 2, "forward row merge pairs two waves per row");
+constexpr int kFwdWaves = FL::kWaves / 4;  // waves per SIMD
+constexpr int kProdWaves = TL::kWaves / 4;
 
 struct Shards {
   int64_t V;
@@ -74,8 +80,8 @@ __device__ __forceinline__ int label_code(int64_t y, int64_t ignore_index,
   return (int)y;
 }
 
-__device__ __forceinline__ int clamp_rows(int64_t remaining) {
-  return remaining <= 0 ? 0 : (remaining >= kTile ? kTile : (int)remaining);
+__device__ __forceinline__ int clamp_rows(int64_t remaining, int cap) {
+  return remaining <= 0 ? 0 : (remaining >= cap ? cap : (int)remaining);
 }
 
 // ---------------------------------------------------------------------------
@@ -95,11 +101,11 @@ struct FwdParams {
 };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
+__global__ __launch_bounds__(FL::kThreads) __attribute__((amdgpu_waves_per_eu(kFwdWaves, kFwdWaves)))
 void fwd_lse_kernel(FwdParams a) {
-  __shared__ __attribute__((aligned(16))) char smem[kGemmLds];
+  __shared__ __attribute__((aligned(16))) char smem[RingOf<FL>::kBytes];
   __shared__ __attribute__((aligned(16))) int lab_s[kTile];
-  __shared__ float xm[TL::WM][TL::R * 64], xs[TL::WM][TL::R * 64];
+  __shared__ float xm[FL::WM][FL::R * 64], xs[FL::WM][FL::R * 64];
 
   const int total = a.T * a.R * a.S;
   const int idx = xcd_remap(blockIdx.x, total);
@@ -109,7 +115,7 @@ void fwd_lse_kernel(FwdParams a) {
   const Shards sh{a.V, a.R};
   const int64_t v0 = a.v_base + sh.begin(r), vw = sh.width(r);
   const int64_t vend = v0 + vw;
-  const int Q = (int)((vw + kTile - 1) / kTile);
+  const int Q = (int)((vw + FL::TN - 1) / FL::TN);
   const int q0 = (int)((int64_t)Q * j / a.S), q1 = (int)((int64_t)Q * (j + 1) / a.S);
 
   const int tid = threadIdx.x;
@@ -120,53 +126,53 @@ void fwd_lse_kernel(FwdParams a) {
                            : kLabIgnored;
   }
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int wm = wave / FL::WN, wn = wave % FL::WN;
   const int p = lane & 31, h = lane >> 5;
 
   const T* Hb = reinterpret_cast<const T*>(a.H) + tok0 * a.d;
-  const int a_rows = clamp_rows(a.N - tok0);
+  const int a_rows = clamp_rows(a.N - tok0, kTile);
 
   // running (max, sum) in base-2 units for row slot p>>1 of each 32-row block
-  float run_m[TL::R], run_s[TL::R];
+  float run_m[FL::R], run_s[FL::R];
 #pragma unroll
-  for (int i = 0; i < TL::R; ++i) { run_m[i] = -INFINITY; run_s[i] = 0.f; }
-  f32x16_t acc[TL::R][TL::C];
+  for (int i = 0; i < FL::R; ++i) { run_m[i] = -INFINITY; run_s[i] = 0.f; }
+  f32x16_t acc[FL::R][FL::C];
 
   for (int q = q0; q < q1; ++q) {
-    const int64_t col0 = v0 + (int64_t)q * kTile;
+    const int64_t col0 = v0 + (int64_t)q * FL::TN;
     const T* Wb = reinterpret_cast<const T*>(a.W) + (col0 - a.v_base) * a.d;
-    tile_mainloop<T>(acc, Hb, a.d, a_rows, Wb, a.d, clamp_rows(vend - col0),
-                     a.d, smem);
-    // columns of this lane: lc + 32*jj, jj = 0..3 (global vocabulary index;
+    tile_mainloop<T, FL>(acc, Hb, a.d, a_rows, Wb, a.d,
+                         clamp_rows(vend - col0, FL::TN), a.d, smem);
+    // columns of this lane: lc + 32*jj, jj = 0..C-1 (global vocabulary index;
     // V < 2^31)
-    const int lc = (int)col0 + wn * TL::kWaveCols + p;
+    const int lc = (int)col0 + wn * FL::kWaveCols + p;
     const int vend32 = (int)vend;
-    bool cv[TL::C];
+    bool cv[FL::C];
 #pragma unroll
-    for (int jj = 0; jj < TL::C; ++jj) cv[jj] = lc + jj * 32 < vend32;
+    for (int jj = 0; jj < FL::C; ++jj) cv[jj] = lc + jj * 32 < vend32;
 
 #pragma unroll
-    for (int i = 0; i < TL::R; ++i) {
+    for (int i = 0; i < FL::R; ++i) {
       float ml[16], sl[16];
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         // 4 consecutive rows: 8*rq + 4*h + (0..3) within the 32-row block
-        const int rowb = wm * TL::kWaveRows + i * 32 + 8 * rq + 4 * h;
+        const int rowb = wm * FL::kWaveRows + i * 32 + 8 * rq + 4 * h;
         const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = rq * 4 + e;
-          float y[TL::C];
+          float y[FL::C];
 #pragma unroll
-          for (int jj = 0; jj < TL::C; ++jj)
+          for (int jj = 0; jj < FL::C; ++jj)
             y[jj] = cv[jj] ? acc[i][jj][rr] * kLog2e : -INFINITY;
           float m = y[0];
 #pragma unroll
-          for (int jj = 1; jj < TL::C; ++jj) m = fmaxf(m, y[jj]);
+          for (int jj = 1; jj < FL::C; ++jj) m = fmaxf(m, y[jj]);
           float s = 0.f;
           if (cv[0]) {
 #pragma unroll
-            for (int jj = 0; jj < TL::C; ++jj) s += fast_exp2(y[jj] - m);
+            for (int jj = 0; jj < FL::C; ++jj) s += fast_exp2(y[jj] - m);
           }
           ml[rr] = m;
           sl[rr] = s;
@@ -174,12 +180,12 @@ void fwd_lse_kernel(FwdParams a) {
           // (label codes of ignored or invalid tokens are negative)
           const int lab = e == 0 ? labs.x : e == 1 ? labs.y : e == 2 ? labs.z : labs.w;
           const int off = lab - lc;
-          if (lab >= 0 && (unsigned)off < (unsigned)TL::kWaveCols &&
+          if (lab >= 0 && (unsigned)off < (unsigned)FL::kWaveCols &&
               (off & 31) == 0 && lab < vend32) {
             const int jsel = off >> 5;
             float z = acc[i][0][rr];
 #pragma unroll
-            for (int jj = 1; jj < TL::C; ++jj)
+            for (int jj = 1; jj < FL::C; ++jj)
               if (jsel == jj) z = acc[i][jj][rr];
             a.tgt[tok0 + rowb + e] = z;
           }
@@ -219,7 +225,7 @@ void fwd_lse_kernel(FwdParams a) {
   // the two waves sharing rows (wn = 0, 1) combine through LDS
   if (wn == 1) {
 #pragma unroll
-    for (int i = 0; i < TL::R; ++i) {
+    for (int i = 0; i < FL::R; ++i) {
       xm[wm][i * 64 + lane] = run_m[i];
       xs[wm][i * 64 + lane] = run_s[i];
     }
@@ -228,10 +234,10 @@ void fwd_lse_kernel(FwdParams a) {
   if (wn == 0 && (p & 1) == 0) {
     const int rr = p >> 1;
 #pragma unroll
-    for (int i = 0; i < TL::R; ++i) {
+    for (int i = 0; i < FL::R; ++i) {
       float m = run_m[i], s = run_s[i];
       ms_merge(m, s, xm[wm][i * 64 + lane], xs[wm][i * 64 + lane]);
-      const int row = wm * TL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+      const int row = wm * FL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
       const int64_t tok = tok0 + row;
       if (tok < a.N) {
         const int64_t o = (int64_t)(r * a.S + j) * a.N + tok;
@@ -395,11 +401,19 @@ __global__ __launch_bounds__(256) void transpose_kernel(
   }
 }
 
-// Transposed G tile staged in LDS (bf16): 256 columns, each 256 tokens long,
-// padded by 16 bytes so that the lanes writing 32 different columns spread
-// over the banks.
+// The bf16 G tile leaves through LDS one wave column (FL::kWaveCols chunk
+// columns, the waves with one wn) at a time. Transposed: each chunk column
+// holds 256 tokens, padded by 16 bytes so that the lanes writing 32 different
+// columns spread over the banks. Row-major: each token row holds the
+// FL::kWaveCols columns, padded the same way.
 constexpr int kGtColBytes = kTile * 2 + 16;
-constexpr int kGtLds = kTile * kGtColBytes;
+constexpr int kGtLds = FL::kWaveCols * kGtColBytes;
+constexpr int kGRowBytes = FL::kWaveCols * 2 + 16;
+constexpr int kGLds = kTile * kGRowBytes;
+constexpr int kRecLds = RingOf<FL>::kBytes > kGtLds
+                            ? (RingOf<FL>::kBytes > kGLds ? RingOf<FL>::kBytes : kGLds)
+                            : (kGtLds > kGLds ? kGtLds : kGLds);
+static_assert(FL::kWaveCols % 8 == 0, "16-byte row chunks");
 
 struct GParams {
   const void* H;
@@ -415,26 +429,23 @@ struct GParams {
   void* GT;              // [C_pad][N_pad]
 };
 
-__device__ __forceinline__ void store_elem(__bf16* p, float v) { *p = (__bf16)v; }
-__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c,
-                                       float d) {
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-  bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
-  *reinterpret_cast<bf16x4_t*>(p) = v;
+// two floats as bf16 (round to nearest even), lo in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c,
                                        float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
+__global__ __launch_bounds__(FL::kThreads) __attribute__((amdgpu_waves_per_eu(kFwdWaves, kFwdWaves)))
 void recompute_g_kernel(GParams a) {
-  // The operand ring, reused after the mainloop as the transposed G tile
-  // (bf16: 256 columns of 256 tokens, padded to kGtColBytes per column).
-  __shared__ __attribute__((aligned(16)))
-  char smem[kGemmLds > kGtLds ? kGemmLds : kGtLds];
+  // The operand ring, reused after the mainloop to stage the bf16 G tile.
+  __shared__ __attribute__((aligned(16))) char smem[kRecLds];
   __shared__ __attribute__((aligned(16))) int lab_s[kTile];
   __shared__ __attribute__((aligned(16))) float lse_s[kTile];
 
@@ -444,113 +455,142 @@ void recompute_g_kernel(GParams a) {
   grouped_tile(idx, a.T, a.CT, kGroupRec, it, ct);
   const int tid = threadIdx.x;
   const int64_t tok0 = (int64_t)it * kTile;
-  const int64_t c0 = (int64_t)ct * kTile;
+  const int64_t c0 = (int64_t)ct * FL::TN;
   if (tid < kTile) {
     const int64_t tok = tok0 + tid;
     lab_s[tid] = tok < a.N ? label_code(a.labels[tok], a.ignore_index, a.V)
                            : kLabIgnored;
     lse_s[tid] = tok < a.N ? a.lse[tok] * kLog2e : 0.f;
   }
-  f32x16_t acc[TL::R][TL::C];
-  tile_mainloop<T>(acc, reinterpret_cast<const T*>(a.H) + tok0 * a.d, a.d,
-                   clamp_rows(a.N - tok0),
-                   reinterpret_cast<const T*>(a.Wc) + c0 * a.d, a.d,
-                   clamp_rows(a.C_eff - c0), a.d, smem);
+  f32x16_t acc[FL::R][FL::C];
+  tile_mainloop<T, FL>(acc, reinterpret_cast<const T*>(a.H) + tok0 * a.d, a.d,
+                       clamp_rows(a.N - tok0, kTile),
+                       reinterpret_cast<const T*>(a.Wc) + c0 * a.d, a.d,
+                       clamp_rows(a.C_eff - c0, FL::TN), a.d, smem);
   const float scale = a.scale[0];
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int wm = wave / FL::WN, wn = wave % FL::WN;
   const int p = lane & 31, h = lane >> 5;
   T* G = reinterpret_cast<T*>(a.G);
   T* GT = reinterpret_cast<T*>(a.GT);
+  // G packed to bf16 pairs (rows 8rq + 4h + 2k, + 1 of block (i, jj) in
+  // gpk[i][jj][2rq + k]), or stored at once (fp32). Chunk columns of this
+  // lane: ccol[jj] = c0 + wn * kWaveCols + jj * 32 + p (< 2^31).
+  uint32_t gpk[FL::R][FL::C][8];
+  int ccol[FL::C];
 #pragma unroll
-  for (int jj = 0; jj < TL::C; ++jj) {
-    const int64_t c = c0 + wn * TL::kWaveCols + jj * 32 + p;  // chunk column
-    const bool cvalid = c < a.C_eff;
-    const bool cstore = c < a.C_pad;
-    const int v = (int)(a.cv0 + c);
+  for (int jj = 0; jj < FL::C; ++jj)
+    ccol[jj] = (int)c0 + wn * FL::kWaveCols + jj * 32 + p;
 #pragma unroll
-    for (int i = 0; i < TL::R; ++i) {
+  for (int i = 0; i < FL::R; ++i) {
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int rowb = wm * TL::kWaveRows + i * 32 + 8 * rq + 4 * h;
-        const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
-        const float4 l2 = *reinterpret_cast<const float4*>(&lse_s[rowb]);
+    for (int rq = 0; rq < 4; ++rq) {
+      const int rowb = wm * FL::kWaveRows + i * 32 + 8 * rq + 4 * h;
+      const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
+      const float4 l2 = *reinterpret_cast<const float4*>(&lse_s[rowb]);
+#pragma unroll
+      for (int jj = 0; jj < FL::C; ++jj) {
+        const int c = ccol[jj];
+        const bool cvalid = c < a.C_eff;
+        const int v = (int)a.cv0 + c;
         float gv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int lab = e == 0 ? labs.x : e == 1 ? labs.y : e == 2 ? labs.z : labs.w;
           const float ls = e == 0 ? l2.x : e == 1 ? l2.y : e == 2 ? l2.z : l2.w;
           const float z = acc[i][jj][rq * 4 + e];
-          float gg = 0.f;
-          if (cvalid && lab != kLabIgnored) {
-            const float pr = fast_exp2(fmaf(z, kLog2e, -ls));
-            gg = scale * (pr - (lab == v ? 1.f : 0.f));
-          }
+          // computed everywhere and selected (no per-element branch); a
+          // discarded value may be NaN, the selected one never is
+          const float pr = fast_exp2(fmaf(z, kLog2e, -ls));
+          const float gg = (cvalid && lab != kLabIgnored)
+                               ? scale * (pr - (lab == v ? 1.f : 0.f))
+                               : 0.f;
           gv[e] = gg;
-          if constexpr (sizeof(T) == 2) {
-            acc[i][jj][rq * 4 + e] = gg;  // kept for the row-major pass
-          } else {
+          if constexpr (sizeof(T) != 2) {
             const int64_t tok = tok0 + rowb + e;
-            if (cstore && tok < a.N) store_elem(G + tok * a.C_pad + c, gg);
+            if (c < a.C_pad && tok < a.N) store_elem(G + tok * a.C_pad + c, gg);
           }
         }
         if constexpr (sizeof(T) == 2) {
-          // column (tile-local) cl, tokens rowb..rowb+3 of the tile
-          const int cl = wn * TL::kWaveCols + jj * 32 + p;
-          store4(reinterpret_cast<T*>(smem + cl * kGtColBytes) + rowb, gv[0],
-                 gv[1], gv[2], gv[3]);
+          gpk[i][jj][2 * rq] = pack_bf16x2(gv[0], gv[1]);
+          gpk[i][jj][2 * rq + 1] = pack_bf16x2(gv[2], gv[3]);
+          // opaque from here on: the compiler would otherwise keep every
+          // unpacked bf16 value alive for the row-major stores and spill
+          asm volatile("" : "+v"(gpk[i][jj][2 * rq]), "+v"(gpk[i][jj][2 * rq + 1]));
         } else {
           const int64_t tokb = tok0 + rowb;
-          if (cstore && tokb < a.N_pad)
-            store4(GT + c * a.N_pad + tokb, gv[0], gv[1], gv[2], gv[3]);
+          if (c < a.C_pad && tokb < a.N_pad)
+            store4(GT + (int64_t)c * a.N_pad + tokb, gv[0], gv[1], gv[2], gv[3]);
         }
       }
     }
   }
   if constexpr (sizeof(T) == 2) {
-    // G^T rows from the transposed tile in LDS: each row of the tile (one
-    // vocabulary column, 256 tokens = 512 bytes) is stored by 32 lanes with
-    // 16-byte stores, coalesced.
-    __syncthreads();
-    constexpr int kChunksPerCol = kTile * 2 / 16;  // 32
-#pragma unroll 4
-    for (int id = tid; id < kTile * kChunksPerCol; id += kThreads) {
-      const int cl = id / kChunksPerCol, u = id % kChunksPerCol;
-      const int64_t c = c0 + cl;
-      const int64_t tokb = tok0 + 8 * u;
-      if (c < a.C_pad && tokb < a.N_pad) {
-        const u32x4_t v =
-            *reinterpret_cast<const u32x4_t*>(smem + cl * kGtColBytes + u * 16);
-        *reinterpret_cast<u32x4_t*>(GT + c * a.N_pad + tokb) = v;
-      }
-    }
-    // G rows: the same tile written row-major (row stride kGtColBytes) from
-    // the values kept in acc, then stored 16 bytes per lane.
-    __syncthreads();
+    __syncthreads();  // every wave is done with the operand ring
+    constexpr int kColChunks = kTile * 2 / 16;          // 16-byte chunks per G^T row
+    constexpr int kRowChunks = FL::kWaveCols * 2 / 16;  // per G row (one pass)
+#pragma unroll 1
+    for (int pass = 0; pass < FL::WN; ++pass) {
+      const int64_t cp0 = c0 + pass * FL::kWaveCols;  // first column of the pass
+      // G^T rows: the waves of this column write their columns transposed
+      // (4 tokens per 8-byte store), then every lane stores 16-byte chunks of
+      // the 256-token rows, coalesced.
+      if (wn == pass) {
 #pragma unroll
-    for (int jj = 0; jj < TL::C; ++jj) {
-      const int cl = wn * TL::kWaveCols + jj * 32 + p;
+        for (int jj = 0; jj < FL::C; ++jj) {
+          const int cl = jj * 32 + p;
 #pragma unroll
-      for (int i = 0; i < TL::R; ++i)
+          for (int i = 0; i < FL::R; ++i)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int row = wm * TL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h +
-                          (rr & 3);
-          store_elem(reinterpret_cast<T*>(smem + row * kGtColBytes) + cl,
-                     acc[i][jj][rr]);
+            for (int rq = 0; rq < 4; ++rq) {
+              const int rowb = wm * FL::kWaveRows + i * 32 + 8 * rq + 4 * h;
+              *reinterpret_cast<u32x2_t*>(smem + cl * kGtColBytes + rowb * 2) =
+                  u32x2_t{gpk[i][jj][2 * rq], gpk[i][jj][2 * rq + 1]};
+            }
         }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int id = tid; id < kTile * kChunksPerCol; id += kThreads) {
-      const int row = id / kChunksPerCol, u = id % kChunksPerCol;
-      const int64_t tok = tok0 + row;
-      const int64_t cc = c0 + 8 * u;
-      if (tok < a.N && cc < a.C_pad) {
-        const u32x4_t v =
-            *reinterpret_cast<const u32x4_t*>(smem + row * kGtColBytes + u * 16);
-        *reinterpret_cast<u32x4_t*>(G + tok * a.C_pad + cc) = v;
       }
+      __syncthreads();
+#pragma unroll 4
+      for (int id = tid; id < FL::kWaveCols * kColChunks; id += FL::kThreads) {
+        const int cl = id / kColChunks, u = id % kColChunks;
+        const int64_t c = cp0 + cl;
+        const int64_t tokb = tok0 + 8 * u;
+        if (c < a.C_pad && tokb < a.N_pad) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+              smem + cl * kGtColBytes + u * 16);
+          *reinterpret_cast<u32x4_t*>(GT + c * a.N_pad + tokb) = v;
+        }
+      }
+      __syncthreads();
+      // G rows: the same columns row-major, then 16-byte chunks per lane.
+      if (wn == pass) {
+#pragma unroll
+        for (int jj = 0; jj < FL::C; ++jj) {
+          const int cl = jj * 32 + p;
+#pragma unroll
+          for (int i = 0; i < FL::R; ++i)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+              const int row = wm * FL::kWaveRows + i * 32 + 8 * (rr >> 2) +
+                              4 * h + (rr & 3);
+              *reinterpret_cast<uint16_t*>(smem + row * kGRowBytes + cl * 2) =
+                  (uint16_t)(gpk[i][jj][rr >> 1] >> (16 * (rr & 1)));
+            }
+        }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int id = tid; id < kTile * kRowChunks; id += FL::kThreads) {
+        const int row = id / kRowChunks, u = id % kRowChunks;
+        const int64_t tok = tok0 + row;
+        const int64_t cc = cp0 + 8 * u;
+        if (tok < a.N && cc < a.C_pad) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+              smem + row * kGRowBytes + u * 16);
+          *reinterpret_cast<u32x4_t*>(G + tok * a.C_pad + cc) = v;
+        }
+      }
+      __syncthreads();
     }
   }
 }
@@ -571,19 +611,19 @@ struct ProdParams {
 };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
+__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(kProdWaves, kProdWaves)))
 void prod_kernel(ProdParams a) {
-  __shared__ __attribute__((aligned(16))) char smem[kGemmLds];
+  __shared__ __attribute__((aligned(16))) char smem[RingOf<TL>::kBytes];
   const int total = a.TM * a.TN;
   const int idx = xcd_remap(blockIdx.x, total);
   int tm, tn;
   grouped_tile(idx, a.TM, a.TN, kGroupBwd, tm, tn);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
   f32x16_t acc[TL::R][TL::C];
-  tile_mainloop<T>(acc, reinterpret_cast<const T*>(a.A) + m0 * a.lda, a.lda,
-                   clamp_rows(a.M - m0),
-                   reinterpret_cast<const T*>(a.B) + n0 * a.ldb, a.ldb,
-                   clamp_rows(a.Nc - n0), a.K, smem);
+  tile_mainloop<T, TL>(acc, reinterpret_cast<const T*>(a.A) + m0 * a.lda,
+                       a.lda, clamp_rows(a.M - m0, kTile),
+                       reinterpret_cast<const T*>(a.B) + n0 * a.ldb, a.ldb,
+                       clamp_rows(a.Nc - n0, kTile), a.K, smem);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
@@ -649,7 +689,7 @@ int32_t check_shape(int64_t N, int64_t d, int64_t V, int32_t R, int32_t dt) {
   if (N < 0 || d < 1 || V < 1 || R < 1 || (int64_t)R > V) return VPCE_ERR_SHAPE;
   // 32-bit buffer offsets: 256 rows of any operand (H^T rows are N long)
   // stay below 2^31 bytes
-  if (V >= ((int64_t)1 << 31) || N > kMaxTokens || d > kMaxTokens)
+  if (V >= ((int64_t)1 << 31) || N > kMaxTokens || d > kMaxHidden)
     return VPCE_ERR_SHAPE;
   if (d % (dt == VPCE_BF16 ? 8 : 4) != 0) return VPCE_ERR_SHAPE;
   // tile indices are int: keep the grids in range
@@ -737,7 +777,7 @@ int32_t run_forward(const Plan& p, const void* H, const void* W,
     FwdParams fp{H, W, labels, p.N, p.d, p.V, ignore_index, p.R, p.S, p.T,
                  pm, ps, tgt, 0, p.V};
     const unsigned grid = (unsigned)((int64_t)p.T * p.R * p.S);
-    hipLaunchKernelGGL(fwd_lse_kernel<T>, dim3(grid), dim3(kThreads), 0, st, fp);
+    hipLaunchKernelGGL(fwd_lse_kernel<T>, dim3(grid), dim3(FL::kThreads), 0, st, fp);
     VPCE_LAUNCH_CHECK();
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)p.nb), dim3(256), 0, st, pm, ps,
                        tgt, labels, p.N, p.R * p.S, ignore_index, lse, bsum, bcnt);
@@ -792,12 +832,12 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
                          p.d, reinterpret_cast<U*>(WT), cpad, cpad);
       VPCE_LAUNCH_CHECK();
     }
-    const int CT = (int)((cpad + kTile - 1) / kTile);
+    const int CT = (int)((cpad + FL::TN - 1) / FL::TN);
     if (p.N > 0) {
       GParams gp{H, Wc, labels, lse, scale, p.N, p.N_pad, p.d, V_lab,
                  ignore_index, cv0, ceff, cpad, p.T, CT, G, GT};
       hipLaunchKernelGGL(recompute_g_kernel<T>, dim3((unsigned)(p.T * CT)),
-                         dim3(kThreads), 0, st, gp);
+                         dim3(FL::kThreads), 0, st, gp);
       VPCE_LAUNCH_CHECK();
     }
     // dW rows of the chunk = G^T H : A = G^T [C_pad x N_pad], B = H^T
@@ -805,7 +845,7 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
       const int TM = (int)((ceff + kTile - 1) / kTile);
       ProdParams pp{GT, p.N_pad, ceff, HT, p.N_pad, p.d, p.N_pad,
                     dWspan + c0 * p.d, p.d, TM, TD, dW_acc ? 1 : 0};
-      hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(TM * TD)), dim3(kThreads), 0,
+      hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(TM * TD)), dim3(TL::kThreads), 0,
                          st, pp);
       VPCE_LAUNCH_CHECK();
     }
@@ -813,7 +853,7 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
     if (p.N > 0) {
       ProdParams pp{G, cpad, p.N, WT, cpad, p.d, cpad, dH, p.d, p.T, TD,
                     acc_h ? 1 : 0};
-      hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(p.T * TD)), dim3(kThreads), 0,
+      hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(p.T * TD)), dim3(TL::kThreads), 0,
                          st, pp);
       VPCE_LAUNCH_CHECK();
     }
@@ -857,7 +897,7 @@ int32_t run_shard_fold(const Plan& p, const void* H, const void* Wshard,
   FwdParams fp{H, Wshard, labels, p.N, p.d, p.V, ignore_index, 1, p.S, p.T,
                pm, ps, state + 2 * p.N, v_begin, V_lab};
   hipLaunchKernelGGL(fwd_lse_kernel<T>, dim3((unsigned)((int64_t)p.T * p.S)),
-                     dim3(kThreads), 0, st, fp);
+                     dim3(FL::kThreads), 0, st, fp);
   VPCE_LAUNCH_CHECK();
   hipLaunchKernelGGL(fold_state_kernel, dim3((unsigned)((p.N + 255) / 256)),
                      dim3(256), 0, st, pm, ps, p.N, p.S, state, state + p.N);
