@@ -435,6 +435,15 @@ __device__ __forceinline__ void grouped_tile(int idx, int tiles_m, int tiles_n,
   tn = off / gs;
 }
 
+// Workgroup barrier that orders LDS accesses only (s_waitcnt lgkmcnt(0);
+// s_barrier): unlike __syncthreads it does not wait for the wave's global
+// stores, which stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }

@@ -526,7 +526,8 @@ void recompute_g_kernel(GParams a) {
     }
   }
   if constexpr (sizeof(T) == 2) {
-    __syncthreads();  // every wave is done with the operand ring
+    // The barriers order the LDS staging only; the G and G^T stores stay in
+    // flight across them and past the end of the workgroup.
     constexpr int kColChunks = kTile * 2 / 16;          // 16-byte chunks per G^T row
     constexpr int kRowChunks = FL::kWaveCols * 2 / 16;  // per G row (one pass)
 #pragma unroll 1
@@ -549,7 +550,7 @@ void recompute_g_kernel(GParams a) {
             }
         }
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll 4
       for (int id = tid; id < FL::kWaveCols * kColChunks; id += FL::kThreads) {
         const int cl = id / kColChunks, u = id % kColChunks;
@@ -561,7 +562,7 @@ void recompute_g_kernel(GParams a) {
           *reinterpret_cast<u32x4_t*>(GT + c * a.N_pad + tokb) = v;
         }
       }
-      __syncthreads();
+      lds_barrier();
       // G rows: the same columns row-major, then 16-byte chunks per lane.
       if (wn == pass) {
 #pragma unroll
@@ -578,7 +579,7 @@ void recompute_g_kernel(GParams a) {
             }
         }
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll 4
       for (int id = tid; id < kTile * kRowChunks; id += FL::kThreads) {
         const int row = id / kRowChunks, u = id % kRowChunks;
@@ -590,7 +591,7 @@ void recompute_g_kernel(GParams a) {
           *reinterpret_cast<u32x4_t*>(G + tok * a.C_pad + cc) = v;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 }
