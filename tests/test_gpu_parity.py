@@ -1,7 +1,9 @@
 """HIP path vs the fp64 oracle, element by element, at sizes the oracle
 finishes in seconds: the tiny fp32 workload, the 4096-token workload, and
-ragged shapes spanning several 256-wide tiles with partial tails in every
-dimension; plus the degenerate cases of the method."""
+ragged shapes spanning several tiles (256 tokens x 320 vocabulary columns in
+the forward and the logit recompute, 256 x 256 in the dW and dH products)
+with partial tails in every dimension; plus the degenerate cases of the
+method."""
 import math
 
 import numpy as np
@@ -65,6 +67,11 @@ RAGGED = [
     (700, 520, 4500, 1, "bf16"),
     (300, 64, 40000, 1, "bf16"),   # one shard over three backward chunks
                                    # (16384 + 16384 + ragged 7232 columns)
+    # shard widths at, above and below the 320-column vocabulary tile
+    (260, 64, 640, 2, "bf16"),     # 320 + 320: whole tiles
+    (300, 136, 963, 3, "bf16"),    # 321 each: a full tile and a 1-column one
+    (257, 72, 1276, 4, "f32"),     # 319 each: one tile, last column empty
+    (129, 96, 3841, 3, "bf16"),    # 1281 / 1280 / 1280: four tiles (+ 1)
 ]
 
 
