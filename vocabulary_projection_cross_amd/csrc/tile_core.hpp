@@ -5,10 +5,11 @@
 // B [Nc x K] are both row-major with K contiguous ("NT" form). Its waves split
 // the tile as Layout<TM, TN, WM, WN> says (4 x 2 waves, two per SIMD, of
 // 64 x 128 on a 256 x 256 tile or 64 x 160 on a 256 x 320 tile); each wave
-// holds its sub-tile as R x C accumulators of the 32x32 MFMA layout:
-//   element r (0..15) of accumulator (i, j) on lane l is
-//   row = i*32 + 8*(r/4) + 4*(l/32) + (r%4),  col = j*32 + (l%32)
-// within the wave's sub-tile.
+// holds its sub-tile as R x C accumulators of MB x MB MFMA blocks (MB = 16 by
+// default, 32 as a build option):
+//   element r of accumulator (i, j) on lane l is
+//   row = i*MB + 8*(r/4) + 4*(l/MB) + (r%4),  col = j*MB + (l%MB)
+// within the wave's sub-tile (MB = 16: r = 0..3; MB = 32: r = 0..15).
 //
 // Operands stream through a ring of NST LDS stages of RB bytes of K per row
 // (128 B x 2 stages by default), copied global -> LDS by buffer loads that
@@ -21,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace vpce {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -30,16 +33,59 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one workgroup on gfx950
 
+// Build-time shape of the engine. Measured on the 1M-context slice: a 2-deep
+// ring of 128-byte slabs is 4% ahead of a 4-deep ring of 64-byte slabs over a
+// full step (whole 128-byte lines per request, a barrier every four K-steps
+// of 32 x 32 blocks instead of two), and 4 x 2 waves ahead of 2 x 2. 64-byte
+// slabs copy 16-row blocks, which a 320-row operand does not split into over
+// 8 waves, so they build only with VPCE_WIDE_COLS=256; for the 256 x 256
+// products (VPCE_PROD_RING_RB/NST) a 3-, 4- or 5-deep ring of 64-byte slabs
+// is 4% slower than the default.
+#ifndef VPCE_WAVES_M
+#define VPCE_WAVES_M 4
+#endif
+#ifndef VPCE_RING_RB
+#define VPCE_RING_RB 128
+#endif
+#ifndef VPCE_RING_NST
+#define VPCE_RING_NST 2
+#endif
+#ifndef VPCE_PROD_RING_RB
+#define VPCE_PROD_RING_RB VPCE_RING_RB
+#endif
+#ifndef VPCE_PROD_RING_NST
+#define VPCE_PROD_RING_NST VPCE_RING_NST
+#endif
+#ifndef VPCE_WIDE_COLS
+#define VPCE_WIDE_COLS 320
+#endif
+// Side of the MFMA output block: 16 (v_mfma_f32_16x16x32_bf16) or 32
+// (v_mfma_f32_32x32x16_bf16). Both have the same nominal rate, but the 16 x 16
+// form reads and writes half the accumulator bytes per flop, and on random
+// bf16 operands the chip, which lowers its clock under MFMA load, holds about
+// 2.0 GHz with it against 1.8 GHz with 32 x 32 blocks. Measured on the
+// 1M-context slice: forward 12% and logit recompute 7% faster with 16 x 16.
+#ifndef VPCE_MFMA_BLOCK
+#define VPCE_MFMA_BLOCK 16
+#endif
+
+
 // Elements of T per 16-byte chunk.
 template <typename T> struct Chunk;
 template <> struct Chunk<__bf16> { static constexpr int E = 8; };
 template <> struct Chunk<float> { static constexpr int E = 4; };
 
 // How the waves of a workgroup split a TM x TN tile: WM x WN waves, each
-// owning a (TM/WM) x (TN/WN) sub-tile held as R x C accumulators of the 32x32
-// MFMA layout. Wave w sits at (w / WN, w % WN). With 8 waves two of them share
+// owning a (TM/WM) x (TN/WN) sub-tile held as R x C accumulators of MB x MB
+// MFMA blocks. Wave w sits at (w / WN, w % WN). With 8 waves two of them share
 // each SIMD, so one wave's MFMAs keep the matrix unit busy while the other
 // waits to issue a copy or an LDS read.
+//
+// Accumulator layout (element r of accumulator (i, j) on lane l), within the
+// wave's sub-tile, for either block side:
+//   row = i*MB + 8*(r/4) + 4*(l/MB) + (r%4),  col = j*MB + (l%MB)
+// (MB = 32: 16 elements, 4 groups of 4 consecutive rows; MB = 16: 4 elements,
+// one group). row_base(i, g, l) is the first of group g's 4 rows.
 //
 // Per K-step a wave runs its R x C MFMAs in NG groups along its longer side
 // (column groups when C > R: group j pairs B fragment j with every A
@@ -47,20 +93,38 @@ template <> struct Chunk<float> { static constexpr int E = 4; };
 // barrier, the stage's copies over those groups. Many small groups issue the
 // copies in small bunches between MFMAs: on a 64 x 160 sub-tile five column
 // groups of two MFMAs take 7% less time than two row groups of five.
-template <int TM_, int TN_, int WM_, int WN_>
+template <int MB> struct AccOf;
+template <> struct AccOf<32> { typedef f32x16_t type; };
+template <> struct AccOf<16> {
+  typedef float type __attribute__((ext_vector_type(4)));
+};
+
+template <int TM_, int TN_, int WM_, int WN_, int MB_ = VPCE_MFMA_BLOCK,
+          int RB_ = VPCE_RING_RB, int NST_ = VPCE_RING_NST>
 struct Layout {
-  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, MB = MB_;
+  static constexpr int RB = RB_, NST = NST_;  // operand ring (see Ring)
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kWaveRows = TM / WM;
   static constexpr int kWaveCols = TN / WN;
-  static constexpr int R = kWaveRows / 32;  // accumulator row blocks
-  static constexpr int C = kWaveCols / 32;  // accumulator column blocks
+  static constexpr int R = kWaveRows / MB;  // accumulator row blocks
+  static constexpr int C = kWaveCols / MB;  // accumulator column blocks
+  static constexpr int kAccRegs = MB * MB / 64;  // fp32 elements per lane
+  static constexpr int kRowGroups = kAccRegs / 4;
+  typedef typename AccOf<MB>::type Acc;
   static constexpr bool kColGroups = C > R;
   static constexpr int NG = kColGroups ? C : R;  // MFMA groups per K-step
+  static_assert(MB == 16 || MB == 32, "MFMA block side");
   static_assert(kWaveRows * WM == TM && kWaveCols * WN == TN &&
-                    kWaveRows % 32 == 0 && kWaveCols % 32 == 0,
-                "whole 32 x 32 blocks per wave");
+                    kWaveRows % MB == 0 && kWaveCols % MB == 0,
+                "whole MFMA blocks per wave");
+  __device__ static constexpr int row_base(int i, int g, int lane) {
+    return i * MB + 8 * g + 4 * (lane / MB);
+  }
+  __device__ static constexpr int col(int j, int lane) {
+    return j * MB + lane % MB;
+  }
 };
 
 // Shape of the operand ring: RB bytes of K per row per stage, NST stages.
@@ -74,7 +138,6 @@ template <int RB, int NST, int TM, int TN, int WAVES>
 struct Ring {
   static_assert(RB == 64 || RB == 128, "row bytes per stage");
   static constexpr int kChunks = RB / 16;              // chunks per row
-  static constexpr int kSteps = RB / 32;               // MFMA K-steps
   static constexpr int kBlockRows = 1024 / RB;         // rows per 1 KiB copy
   static constexpr int kBlocksA = TM / kBlockRows / WAVES;  // per wave
   static constexpr int kBlocksB = TN / kBlockRows / WAVES;
@@ -95,43 +158,65 @@ struct Ring {
 
 // One K-step of MFMA group q (see Layout): row group q updates accumulators
 // (q, 0..C-1), column group q updates (0..R-1, q). Each lane supplies 16
-// bytes of A and 16 bytes of B per 32 x 32 block.
-//   bf16: one v_mfma_f32_32x32x16_bf16 per accumulator (lane half h carries
-//         k = 8h..8h+7 of the step's 16).
-//   fp32: four v_mfma_f32_32x32x2_f32 per accumulator; instruction e pairs
-//         element e of the two halves' chunks. Any pairing of k between A and
-//         B that is the same on both operands gives the same sum.
+// bytes of A and 16 bytes of B per MFMA block; lane l serves row l % MB of
+// the block and K-chunk l / MB of the step's 64 / MB chunks.
+//   bf16, MB = 32: one v_mfma_f32_32x32x16_bf16 per accumulator (K = 16).
+//   bf16, MB = 16: one v_mfma_f32_16x16x32_bf16 per accumulator (K = 32).
+//   fp32: four v_mfma_f32_32x32x2_f32 (16x16x4_f32) per accumulator;
+//         instruction e pairs element e of every lane's chunk. Any pairing of
+//         k between A and B that is the same on both operands gives the same
+//         sum.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename L>
-__device__ __forceinline__ void mma_group(f32x16_t (&acc)[L::R][L::C],
-                                          const u32x4_t (&a)[L::R],
-                                          const u32x4_t (&b)[L::C], int q,
-                                          const __bf16*) {
-  constexpr int GS = L::kColGroups ? L::R : L::C;
-#pragma unroll
-  for (int g = 0; g < GS; ++g) {
-    const int i = L::kColGroups ? g : q, j = L::kColGroups ? q : g;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, b[j]),
-        acc[i][j], 0, 0, 0);
-  }
+__device__ __forceinline__ typename L::Acc mfma_block(const u32x4_t& a,
+                                                      const u32x4_t& b,
+                                                      typename L::Acc c,
+                                                      const __bf16*) {
+  if constexpr (L::MB == 32)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+        0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+        0, 0, 0);
 }
+// fp32: element e of both chunks (one step of four; see mma_group).
 template <typename L>
-__device__ __forceinline__ void mma_group(f32x16_t (&acc)[L::R][L::C],
+__device__ __forceinline__ typename L::Acc mfma_block_f32(float a, float b,
+                                                          typename L::Acc c) {
+  if constexpr (L::MB == 32)
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename L, typename T>
+__device__ __forceinline__ void mma_group(typename L::Acc (&acc)[L::R][L::C],
                                           const u32x4_t (&a)[L::R],
                                           const u32x4_t (&b)[L::C], int q,
-                                          const float*) {
+                                          const T* tag) {
   constexpr int GS = L::kColGroups ? L::R : L::C;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
       const int i = L::kColGroups ? g : q, j = L::kColGroups ? q : g;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-          __builtin_bit_cast(f32x4_t, a[i])[e],
-          __builtin_bit_cast(f32x4_t, b[j])[e], acc[i][j], 0, 0, 0);
+      acc[i][j] = mfma_block<L>(a[i], b[j], acc[i][j], tag);
     }
+  } else {
+    // the four instructions of one accumulator are interleaved with the
+    // group's other accumulators, so consecutive MFMAs are independent
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        const int i = L::kColGroups ? g : q, j = L::kColGroups ? q : g;
+        acc[i][j] = mfma_block_f32<L>(__builtin_bit_cast(f32x4_t, a[i])[e],
+                                      __builtin_bit_cast(f32x4_t, b[j])[e],
+                                      acc[i][j]);
+      }
+  }
 }
 
 typedef __attribute__((address_space(3))) char lds_char_t;
@@ -197,25 +282,27 @@ constexpr int waitcnt_vm_lgkm(int vm, int lgkm) {
 // buffer stage kt leaves (see the loop for why that order is safe).
 template <typename T, typename L, int RB, int NST>
 __device__ __forceinline__ void tile_mainloop_ring(
-    f32x16_t (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
+    typename L::Acc (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
     int a_rows, const T* __restrict__ B, int64_t ldb, int b_rows, int64_t K,
     char* smem) {
   using P = Ring<RB, NST, L::TM, L::TN, L::kWaves>;
-  constexpr int R = L::R, C = L::C, NG = L::NG;
+  constexpr int R = L::R, C = L::C, NG = L::NG, MB = L::MB;
   constexpr int E = Chunk<T>::E;           // elements per 16-byte chunk
   constexpr int BK = RB / (int)sizeof(T);  // elements of K per stage
-  constexpr int S = P::kSteps;
+  constexpr int CPS = 64 / MB;             // 16-byte chunks per K-step
+  constexpr int S = P::kChunks / CPS;      // K-steps per stage
+  static_assert(S >= 1 && S * CPS == P::kChunks, "whole K-steps per stage");
   constexpr int KA = P::kBlocksA, KB = P::kBlocksB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int swave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
   const int wm = wave / L::WN, wn = wave % L::WN;
-  const int p = lane & 31, h = lane >> 5;
+  const int p = lane % MB, h = lane / MB;
 #pragma unroll
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int j = 0; j < C; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < L::kAccRegs; ++r) acc[i][j][r] = 0.f;
 
   const int KT = (int)((K + BK - 1) / BK);
   if (KT <= 0) return;
@@ -280,63 +367,32 @@ __device__ __forceinline__ void tile_mainloop_ring(
       copy16_to_lds(dstb + boff, vb[e] + rows * pb, rsb);
   };
 
-  // fragment side: lane (p, h) reads row (base + 32*i + p) at chunk 2s + h;
-  // rows differ from p by multiples of 32, so the swizzle is swz(p).
+  // fragment side: lane (p, h) reads row (base + MB*i + p) at chunk
+  // CPS*s + h; rows differ from p by multiples of MB (16 or 32), so the
+  // swizzle is swz(p).
   const int g = P::swz(p);
   const int fa = (wm * L::kWaveRows + p) * RB;
   const int fb = P::kOperandBytesA + (wn * L::kWaveCols + p) * RB;
   int fo[S];
 #pragma unroll
-  for (int st = 0; st < S; ++st) fo[st] = ((2 * st + h) ^ g) << 4;
-  u32x4_t af[2][R], bfr[2][C];
-  // read number n of a step's R + C fragment reads, in the order the groups
-  // need them: row groups A0, B0..B(C-1), A1..A(R-1); column groups B0,
-  // A0..A(R-1), B1..B(C-1)
-  constexpr int kReads = R + C;
-  auto read_one = [&](int stage_off, int st, int buf, int n) {
-    bool is_a;
-    int x;
-    if (!L::kColGroups) {
-      is_a = n == 0 || n > C;
-      x = n == 0 ? 0 : (n > C ? n - C : n - 1);
-    } else {
-      is_a = n >= 1 && n <= R;
-      x = n == 0 ? 0 : (n <= R ? n - 1 : n - R);
-    }
-    if (is_a)
-      af[buf][x] = *reinterpret_cast<const u32x4_t*>(
-          smem + stage_off + fa + fo[st] + x * 32 * RB);
-    else
-      bfr[buf][x] = *reinterpret_cast<const u32x4_t*>(
-          smem + stage_off + fb + fo[st] + x * 32 * RB);
+  for (int st = 0; st < S; ++st) fo[st] = ((CPS * st + h) ^ g) << 4;
+  auto frag_a = [&](int stage_off, int st, int x) {
+    return *reinterpret_cast<const u32x4_t*>(smem + stage_off + fa + fo[st] +
+                                             x * MB * RB);
   };
-  // reads [n0, n1) of a step
-  auto reads = [&](int stage_off, int st, int buf, int n0, int n1) {
-#pragma unroll
-    for (int n = 0; n < kReads; ++n)
-      if (n >= n0 && n < n1) read_one(stage_off, st, buf, n);
+  auto frag_b = [&](int stage_off, int st, int x) {
+    return *reinterpret_cast<const u32x4_t*>(smem + stage_off + fb + fo[st] +
+                                             x * MB * RB);
   };
-
-  for (int st = 0; st < NST; ++st) {
-    stage_offsets(st);
-#pragma unroll
-    for (int c = 0; c < P::kCopies; ++c) copy_one(st, c);
-  }
-  // stage 0 landed (the copies of stages 1 .. NST-1 may stay outstanding)
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm((NST - 1) * P::kCopies, 15));
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  reads(0, 0, 0, 0, kReads);
   const T* tag = nullptr;
 
-  // Each step's fragment reads are spread over the previous step's groups
-  // (the first group's fragments first). The last step of stage kt opens
-  // with the barrier, which waits until this wave's copies of stage kt + 1
-  // have landed and its own LDS reads have completed: after it every wave
-  // holds stage kt's fragments in registers, so buffer kt % NST is free and
-  // the wave issues its copies of stage kt + NST into it while reading stage
-  // kt + 1's first fragments. Copies of stages kt + 2 .. kt + NST - 1 may
-  // stay outstanding at the barrier.
+  // The last step of stage kt opens with the barrier, which waits until this
+  // wave's copies of stage kt + 1 have landed and its own LDS reads have
+  // completed: after it every wave holds stage kt's last fragments in
+  // registers, so buffer kt % NST is free and the wave issues its copies of
+  // stage kt + NST into it while reading stage kt + 1's first fragments.
+  // Copies of stages kt + 2 .. kt + NST - 1 may stay outstanding at the
+  // barrier.
   constexpr int kVmAllowed = (NST - 2) * P::kCopies;
   static_assert((NST - 1) * P::kCopies <= 63, "vmcnt range");
   auto copies_at = [&](int s, int grp) {
@@ -344,31 +400,132 @@ __device__ __forceinline__ void tile_mainloop_ring(
     for (int c = 0; c < P::kCopies; ++c)
       if (c * NG / P::kCopies == grp) copy_one(s, c);
   };
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = (kt % NST) * P::kStageBytes;
-    const int nxt = ((kt + 1) % NST) * P::kStageBytes;
+  auto prologue = [&]() {
+    for (int st = 0; st < NST; ++st) {
+      stage_offsets(st);
 #pragma unroll
-    for (int st = 0; st < S - 1; ++st) {
+      for (int c = 0; c < P::kCopies; ++c) copy_one(st, c);
+    }
+    // stage 0 landed (the copies of stages 1 .. NST-1 may stay outstanding)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm((NST - 1) * P::kCopies, 15));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if constexpr (MB == 32) {
+    // Two fragment sets by step parity: each step's R + C reads are spread
+    // over the previous step's groups (the first group's fragments first).
+    u32x4_t af[2][R], bfr[2][C];
+    // read number n of a step's R + C fragment reads, in the order the
+    // groups need them: row groups A0, B0..B(C-1), A1..A(R-1); column groups
+    // B0, A0..A(R-1), B1..B(C-1)
+    constexpr int kReads = R + C;
+    auto read_one = [&](int stage_off, int st, int buf, int n) {
+      bool is_a;
+      int x;
+      if (!L::kColGroups) {
+        is_a = n == 0 || n > C;
+        x = n == 0 ? 0 : (n > C ? n - C : n - 1);
+      } else {
+        is_a = n >= 1 && n <= R;
+        x = n == 0 ? 0 : (n <= R ? n - 1 : n - R);
+      }
+      if (is_a)
+        af[buf][x] = frag_a(stage_off, st, x);
+      else
+        bfr[buf][x] = frag_b(stage_off, st, x);
+    };
+    // reads [n0, n1) of a step
+    auto reads = [&](int stage_off, int st, int buf, int n0, int n1) {
+#pragma unroll
+      for (int n = 0; n < kReads; ++n)
+        if (n >= n0 && n < n1) read_one(stage_off, st, buf, n);
+    };
+    prologue();
+    reads(0, 0, 0, 0, kReads);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = (kt % NST) * P::kStageBytes;
+      const int nxt = ((kt + 1) % NST) * P::kStageBytes;
+#pragma unroll
+      for (int st = 0; st < S - 1; ++st) {
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          reads(cur, st + 1, (st + 1) & 1, q * kReads / NG,
+                (q + 1) * kReads / NG);
+          mma_group<L>(acc, af[st & 1], bfr[st & 1], q, tag);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      constexpr int LB = (S - 1) & 1;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kVmAllowed, 0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      stage_offsets(kt + NST);
 #pragma unroll
       for (int q = 0; q < NG; ++q) {
-        reads(cur, st + 1, (st + 1) & 1, q * kReads / NG,
-              (q + 1) * kReads / NG);
-        mma_group<L>(acc, af[st & 1], bfr[st & 1], q, tag);
+        reads(nxt, 0, 0, q * kReads / NG, (q + 1) * kReads / NG);
+        copies_at(kt + NST, q);
+        mma_group<L>(acc, af[LB], bfr[LB], q, tag);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    constexpr int LB = (S - 1) & 1;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kVmAllowed, 0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    stage_offsets(kt + NST);
+  } else {
+    // MB = 16, column groups: every group uses all R A-fragments, group q
+    // B-fragment q. A has two sets by step parity (the next step's A is read
+    // during the current step, in its first R groups); B has one set,
+    // refilled in place: right after group q's MFMAs the wave reads the next
+    // step's B fragment q into it, so a step holds R + C fragments of its own
+    // plus R of the next (a second B set would not fit beside 160
+    // accumulator registers). With an odd number of steps per stage the
+    // stages alternate in which A set they start with, so the stage loop runs
+    // two stages per iteration.
+    static_assert(L::kColGroups, "16 x 16 blocks: column groups");
+    u32x4_t af[2][R], bfr[C];
+    prologue();
 #pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      reads(nxt, 0, 0, q * kReads / NG, (q + 1) * kReads / NG);
-      copies_at(kt + NST, q);
-      mma_group<L>(acc, af[LB], bfr[LB], q, tag);
+    for (int x = 0; x < C; ++x) bfr[x] = frag_b(0, 0, x);
+#pragma unroll
+    for (int x = 0; x < R; ++x) af[0][x] = frag_a(0, 0, x);
+    // stage kt, whose first step uses A set A0
+    auto run_stage = [&](int kt, auto a0) {
+      constexpr int A0 = decltype(a0)::value;
+      const int cur = (kt % NST) * P::kStageBytes;
+      const int nxt = ((kt + 1) % NST) * P::kStageBytes;
+#pragma unroll
+      for (int st = 0; st < S - 1; ++st) {
+        const int as = (A0 + st) & 1;
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+          mma_group<L>(acc, af[as], bfr, q, tag);
+          __builtin_amdgcn_sched_barrier(0);
+          bfr[q] = frag_b(cur, st + 1, q);
+          if (q < R) af[as ^ 1][q] = frag_a(cur, st + 1, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      constexpr int LB = (A0 + S - 1) & 1;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kVmAllowed, 0));
+      __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
+      stage_offsets(kt + NST);
+#pragma unroll
+      for (int q = 0; q < C; ++q) {
+        mma_group<L>(acc, af[LB], bfr, q, tag);
+        __builtin_amdgcn_sched_barrier(0);
+        bfr[q] = frag_b(nxt, 0, q);
+        if (q < R) af[LB ^ 1][q] = frag_a(nxt, 0, q);
+        copies_at(kt + NST, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if constexpr (S % 2 == 0) {
+      for (int kt = 0; kt < KT; ++kt)
+        run_stage(kt, std::integral_constant<int, 0>{});
+    } else {
+      for (int kt = 0; kt < KT; kt += 2) {
+        run_stage(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < KT) run_stage(kt + 1, std::integral_constant<int, 1>{});
+      }
     }
   }
   // drain the copies issued past K before smem is reused
@@ -377,40 +534,22 @@ __device__ __forceinline__ void tile_mainloop_ring(
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Build-time shape of the engine. Measured on the 1M-context slice: a 2-deep
-// ring of 128-byte slabs is 4% ahead of a 4-deep ring of 64-byte slabs over a
-// full step (whole 128-byte lines per request, a barrier every four K-steps
-// instead of two), and 4 x 2 waves ahead of 2 x 2. 64-byte slabs copy 16-row
-// blocks, which a 320-row operand does not split into over 8 waves, so they
-// build only with VPCE_WIDE_COLS=256.
-#ifndef VPCE_WAVES_M
-#define VPCE_WAVES_M 4
-#endif
-#ifndef VPCE_RING_RB
-#define VPCE_RING_RB 128
-#endif
-#ifndef VPCE_RING_NST
-#define VPCE_RING_NST 2
-#endif
-#ifndef VPCE_WIDE_COLS
-#define VPCE_WIDE_COLS 320
-#endif
-
 // The two configurations: 256 x 256 tiles for the dW and dH products (whose
 // output dimensions are multiples of 256 in the usual shapes), 256 x 320 tiles
 // (vocabulary on the 320 side) for the forward and the logit recompute.
-using TileLayout = Layout<256, 256, VPCE_WAVES_M, 2>;
+using TileLayout = Layout<256, 256, VPCE_WAVES_M, 2, VPCE_MFMA_BLOCK,
+                          VPCE_PROD_RING_RB, VPCE_PROD_RING_NST>;
 using WideLayout = Layout<256, VPCE_WIDE_COLS, 4, 2>;
 template <typename L>
-using RingOf = Ring<VPCE_RING_RB, VPCE_RING_NST, L::TM, L::TN, L::kWaves>;
+using RingOf = Ring<L::RB, L::NST, L::TM, L::TN, L::kWaves>;
 
 // smem must hold RingOf<L>::kBytes.
 template <typename T, typename L>
 __device__ __forceinline__ void tile_mainloop(
-    f32x16_t (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
+    typename L::Acc (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
     int a_rows, const T* __restrict__ B, int64_t ldb, int b_rows, int64_t K,
     char* smem) {
-  tile_mainloop_ring<T, L, VPCE_RING_RB, VPCE_RING_NST>(
+  tile_mainloop_ring<T, L, L::RB, L::NST>(
       acc, A, lda, a_rows, B, ldb, b_rows, K, smem);
 }
 

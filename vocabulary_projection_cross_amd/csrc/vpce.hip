@@ -100,12 +100,25 @@ struct FwdParams {
   int64_t V_lab;   // labels outside [0, V_lab) (and not ignored) are invalid
 };
 
+// Row reduction of the forward epilogue. A lane holds 16 row values of a
+// "unit" of accumulator row blocks (one 32-row block for MB = 32, four 16-row
+// blocks for MB = 16); the lanes that share those rows (the MB lanes of a
+// lane group) reduce-scatter them, after which lane l holds fully reduced
+// value k(l) of the unit (MB = 32: k = (l % 32) / 2, lanes l and l ^ 1 alike;
+// MB = 16: k = l % 16). Value k is element k % kAccRegs of row block
+// k / kAccRegs of the unit.
+constexpr int kUnitBlocks = FL::MB == 32 ? 1 : 16 / FL::kAccRegs;
+constexpr int kUnits = FL::R / kUnitBlocks;  // units per wave
+static_assert(kUnitBlocks * FL::kAccRegs == 16 && kUnits * kUnitBlocks == FL::R,
+              "16 row values per unit");
+
 template <typename T>
 __global__ __launch_bounds__(FL::kThreads) __attribute__((amdgpu_waves_per_eu(kFwdWaves, kFwdWaves)))
 void fwd_lse_kernel(FwdParams a) {
   __shared__ __attribute__((aligned(16))) char smem[RingOf<FL>::kBytes];
   __shared__ __attribute__((aligned(16))) int lab_s[kTile];
-  __shared__ float xm[FL::WM][FL::R * 64], xs[FL::WM][FL::R * 64];
+  __shared__ float xm[FL::WM][kUnits * 64], xs[FL::WM][kUnits * 64];
+  constexpr int MB = FL::MB;
 
   const int total = a.T * a.R * a.S;
   const int idx = xcd_remap(blockIdx.x, total);
@@ -127,72 +140,77 @@ void fwd_lse_kernel(FwdParams a) {
   }
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / FL::WN, wn = wave % FL::WN;
-  const int p = lane & 31, h = lane >> 5;
+  const int p = lane % MB;
 
   const T* Hb = reinterpret_cast<const T*>(a.H) + tok0 * a.d;
   const int a_rows = clamp_rows(a.N - tok0, kTile);
 
-  // running (max, sum) in base-2 units for row slot p>>1 of each 32-row block
-  float run_m[FL::R], run_s[FL::R];
+  // running (max, sum) in base-2 units of this lane's reduced value k(lane)
+  // of each unit
+  float run_m[kUnits], run_s[kUnits];
 #pragma unroll
-  for (int i = 0; i < FL::R; ++i) { run_m[i] = -INFINITY; run_s[i] = 0.f; }
-  f32x16_t acc[FL::R][FL::C];
+  for (int u = 0; u < kUnits; ++u) { run_m[u] = -INFINITY; run_s[u] = 0.f; }
+  typename FL::Acc acc[FL::R][FL::C];
 
   for (int q = q0; q < q1; ++q) {
     const int64_t col0 = v0 + (int64_t)q * FL::TN;
     const T* Wb = reinterpret_cast<const T*>(a.W) + (col0 - a.v_base) * a.d;
     tile_mainloop<T, FL>(acc, Hb, a.d, a_rows, Wb, a.d,
                          clamp_rows(vend - col0, FL::TN), a.d, smem);
-    // columns of this lane: lc + 32*jj, jj = 0..C-1 (global vocabulary index;
-    // V < 2^31)
-    const int lc = (int)col0 + wn * FL::kWaveCols + p;
+    // columns of this lane: lc + MB*jj, jj = 0..C-1 (global vocabulary
+    // index; V < 2^31)
+    const int lc = (int)col0 + wn * FL::kWaveCols + FL::col(0, lane);
     const int vend32 = (int)vend;
     bool cv[FL::C];
 #pragma unroll
-    for (int jj = 0; jj < FL::C; ++jj) cv[jj] = lc + jj * 32 < vend32;
+    for (int jj = 0; jj < FL::C; ++jj) cv[jj] = lc + jj * MB < vend32;
 
 #pragma unroll
-    for (int i = 0; i < FL::R; ++i) {
+    for (int u = 0; u < kUnits; ++u) {
       float ml[16], sl[16];
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        // 4 consecutive rows: 8*rq + 4*h + (0..3) within the 32-row block
-        const int rowb = wm * FL::kWaveRows + i * 32 + 8 * rq + 4 * h;
-        const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
+      for (int ib = 0; ib < kUnitBlocks; ++ib) {
+        const int i = u * kUnitBlocks + ib;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = rq * 4 + e;
-          float y[FL::C];
+        for (int rg = 0; rg < FL::kRowGroups; ++rg) {
+          // 4 consecutive rows of this lane
+          const int rowb = wm * FL::kWaveRows + FL::row_base(i, rg, lane);
+          const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
 #pragma unroll
-          for (int jj = 0; jj < FL::C; ++jj)
-            y[jj] = cv[jj] ? acc[i][jj][rr] * kLog2e : -INFINITY;
-          float m = y[0];
+          for (int e = 0; e < 4; ++e) {
+            const int rr = rg * 4 + e;              // element of acc[i][.]
+            const int k = ib * FL::kAccRegs + rr;   // value of the unit
+            float y[FL::C];
 #pragma unroll
-          for (int jj = 1; jj < FL::C; ++jj) m = fmaxf(m, y[jj]);
-          float s = 0.f;
-          if (cv[0]) {
+            for (int jj = 0; jj < FL::C; ++jj)
+              y[jj] = cv[jj] ? acc[i][jj][rr] * kLog2e : -INFINITY;
+            float m = y[0];
 #pragma unroll
-            for (int jj = 0; jj < FL::C; ++jj) s += fast_exp2(y[jj] - m);
-          }
-          ml[rr] = m;
-          sl[rr] = s;
-          // target logit: the label's column is lc + 32*jj for some jj
-          // (label codes of ignored or invalid tokens are negative)
-          const int lab = e == 0 ? labs.x : e == 1 ? labs.y : e == 2 ? labs.z : labs.w;
-          const int off = lab - lc;
-          if (lab >= 0 && (unsigned)off < (unsigned)FL::kWaveCols &&
-              (off & 31) == 0 && lab < vend32) {
-            const int jsel = off >> 5;
-            float z = acc[i][0][rr];
+            for (int jj = 1; jj < FL::C; ++jj) m = fmaxf(m, y[jj]);
+            float s = 0.f;
+            if (cv[0]) {
 #pragma unroll
-            for (int jj = 1; jj < FL::C; ++jj)
-              if (jsel == jj) z = acc[i][jj][rr];
-            a.tgt[tok0 + rowb + e] = z;
+              for (int jj = 0; jj < FL::C; ++jj) s += fast_exp2(y[jj] - m);
+            }
+            ml[k] = m;
+            sl[k] = s;
+            // target logit: the label's column is lc + MB*jj for some jj
+            // (label codes of ignored or invalid tokens are negative)
+            const int lab = e == 0 ? labs.x : e == 1 ? labs.y : e == 2 ? labs.z : labs.w;
+            const int off = lab - lc;
+            if (lab >= 0 && (unsigned)off < (unsigned)FL::kWaveCols &&
+                (off % MB) == 0 && lab < vend32) {
+              const int jsel = off / MB;
+              float z = acc[i][0][rr];
+#pragma unroll
+              for (int jj = 1; jj < FL::C; ++jj)
+                if (jsel == jj) z = acc[i][jj][rr];
+              a.tgt[tok0 + rowb + e] = z;
+            }
           }
         }
       }
-      // reduce-scatter the 16 row states across the 32 lanes of each half;
-      // afterwards lanes p and p^1 both hold row slot p>>1, fully reduced.
+      // reduce-scatter the 16 row values across the lanes that share them
 #define VPCE_RS_STEP(MASK, HALF)                                        \
       {                                                                 \
         const bool upper = (p & (MASK)) != 0;                           \
@@ -207,17 +225,22 @@ void fwd_lse_kernel(FwdParams a) {
           sl[k] = s;                                                    \
         }                                                               \
       }
-      VPCE_RS_STEP(16, 8)
-      VPCE_RS_STEP(8, 4)
-      VPCE_RS_STEP(4, 2)
-      VPCE_RS_STEP(2, 1)
-#undef VPCE_RS_STEP
-      {
+      if constexpr (MB == 32) {
+        VPCE_RS_STEP(16, 8)
+        VPCE_RS_STEP(8, 4)
+        VPCE_RS_STEP(4, 2)
+        VPCE_RS_STEP(2, 1)
         const float mo = half_xor<1>(ml[0]);
         const float so = half_xor<1>(sl[0]);
         ms_merge(ml[0], sl[0], mo, so);
+      } else {
+        VPCE_RS_STEP(8, 8)
+        VPCE_RS_STEP(4, 4)
+        VPCE_RS_STEP(2, 2)
+        VPCE_RS_STEP(1, 1)
       }
-      ms_merge(run_m[i], run_s[i], ml[0], sl[0]);
+#undef VPCE_RS_STEP
+      ms_merge(run_m[u], run_s[u], ml[0], sl[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -225,19 +248,21 @@ void fwd_lse_kernel(FwdParams a) {
   // the two waves sharing rows (wn = 0, 1) combine through LDS
   if (wn == 1) {
 #pragma unroll
-    for (int i = 0; i < FL::R; ++i) {
-      xm[wm][i * 64 + lane] = run_m[i];
-      xs[wm][i * 64 + lane] = run_s[i];
+    for (int u = 0; u < kUnits; ++u) {
+      xm[wm][u * 64 + lane] = run_m[u];
+      xs[wm][u * 64 + lane] = run_s[u];
     }
   }
   __syncthreads();
-  if (wn == 0 && (p & 1) == 0) {
-    const int rr = p >> 1;
+  const int kred = MB == 32 ? (p >> 1) : p;  // reduced value of this lane
+  if (wn == 0 && (MB == 16 || (p & 1) == 0)) {
+    const int ib = kred / FL::kAccRegs, rr = kred % FL::kAccRegs;
 #pragma unroll
-    for (int i = 0; i < FL::R; ++i) {
-      float m = run_m[i], s = run_s[i];
-      ms_merge(m, s, xm[wm][i * 64 + lane], xs[wm][i * 64 + lane]);
-      const int row = wm * FL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+    for (int u = 0; u < kUnits; ++u) {
+      float m = run_m[u], s = run_s[u];
+      ms_merge(m, s, xm[wm][u * 64 + lane], xs[wm][u * 64 + lane]);
+      const int row = wm * FL::kWaveRows +
+                      FL::row_base(u * kUnitBlocks + ib, rr / 4, lane) + rr % 4;
       const int64_t tok = tok0 + row;
       if (tok < a.N) {
         const int64_t o = (int64_t)(r * a.S + j) * a.N + tok;
@@ -462,7 +487,7 @@ void recompute_g_kernel(GParams a) {
                            : kLabIgnored;
     lse_s[tid] = tok < a.N ? a.lse[tok] * kLog2e : 0.f;
   }
-  f32x16_t acc[FL::R][FL::C];
+  typename FL::Acc acc[FL::R][FL::C];
   tile_mainloop<T, FL>(acc, reinterpret_cast<const T*>(a.H) + tok0 * a.d, a.d,
                        clamp_rows(a.N - tok0, kTile),
                        reinterpret_cast<const T*>(a.Wc) + c0 * a.d, a.d,
@@ -470,22 +495,21 @@ void recompute_g_kernel(GParams a) {
   const float scale = a.scale[0];
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / FL::WN, wn = wave % FL::WN;
-  const int p = lane & 31, h = lane >> 5;
   T* G = reinterpret_cast<T*>(a.G);
   T* GT = reinterpret_cast<T*>(a.GT);
-  // G packed to bf16 pairs (rows 8rq + 4h + 2k, + 1 of block (i, jj) in
-  // gpk[i][jj][2rq + k]), or stored at once (fp32). Chunk columns of this
-  // lane: ccol[jj] = c0 + wn * kWaveCols + jj * 32 + p (< 2^31).
-  uint32_t gpk[FL::R][FL::C][8];
+  // G packed to bf16 pairs (rows 2k, 2k + 1 of row group rq of accumulator
+  // (i, jj) in gpk[i][jj][2rq + k]), or stored at once (fp32). Chunk columns
+  // of this lane: ccol[jj] = c0 + wn * kWaveCols + col(jj) (< 2^31).
+  uint32_t gpk[FL::R][FL::C][FL::kAccRegs / 2];
   int ccol[FL::C];
 #pragma unroll
   for (int jj = 0; jj < FL::C; ++jj)
-    ccol[jj] = (int)c0 + wn * FL::kWaveCols + jj * 32 + p;
+    ccol[jj] = (int)c0 + wn * FL::kWaveCols + FL::col(jj, lane);
 #pragma unroll
   for (int i = 0; i < FL::R; ++i) {
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int rowb = wm * FL::kWaveRows + i * 32 + 8 * rq + 4 * h;
+    for (int rq = 0; rq < FL::kRowGroups; ++rq) {
+      const int rowb = wm * FL::kWaveRows + FL::row_base(i, rq, lane);
       const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
       const float4 l2 = *reinterpret_cast<const float4*>(&lse_s[rowb]);
 #pragma unroll
@@ -539,12 +563,12 @@ void recompute_g_kernel(GParams a) {
       if (wn == pass) {
 #pragma unroll
         for (int jj = 0; jj < FL::C; ++jj) {
-          const int cl = jj * 32 + p;
+          const int cl = FL::col(jj, lane);
 #pragma unroll
           for (int i = 0; i < FL::R; ++i)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-              const int rowb = wm * FL::kWaveRows + i * 32 + 8 * rq + 4 * h;
+            for (int rq = 0; rq < FL::kRowGroups; ++rq) {
+              const int rowb = wm * FL::kWaveRows + FL::row_base(i, rq, lane);
               *reinterpret_cast<u32x2_t*>(smem + cl * kGtColBytes + rowb * 2) =
                   u32x2_t{gpk[i][jj][2 * rq], gpk[i][jj][2 * rq + 1]};
             }
@@ -567,13 +591,13 @@ void recompute_g_kernel(GParams a) {
       if (wn == pass) {
 #pragma unroll
         for (int jj = 0; jj < FL::C; ++jj) {
-          const int cl = jj * 32 + p;
+          const int cl = FL::col(jj, lane);
 #pragma unroll
           for (int i = 0; i < FL::R; ++i)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-              const int row = wm * FL::kWaveRows + i * 32 + 8 * (rr >> 2) +
-                              4 * h + (rr & 3);
+            for (int rr = 0; rr < FL::kAccRegs; ++rr) {
+              const int row = wm * FL::kWaveRows +
+                              FL::row_base(i, rr >> 2, lane) + (rr & 3);
               *reinterpret_cast<uint16_t*>(smem + row * kGRowBytes + cl * 2) =
                   (uint16_t)(gpk[i][jj][rr >> 1] >> (16 * (rr & 1)));
             }
@@ -595,6 +619,13 @@ void recompute_g_kernel(GParams a) {
     }
   }
 }
+
+// Output staging of the products: a band of 64 tile rows in fp32, rows padded
+// by 16 bytes (the lanes of one accumulator write hit 64 distinct banks).
+constexpr int kProdBandRows = TL::kWaveRows;
+constexpr int kProdPitch = TL::TN * 4 + 16;
+static_assert(kProdBandRows * kProdPitch <= RingOf<TL>::kBytes,
+              "a band fits the operand ring");
 
 // out[M x Nc] (row stride ldo) = A . B^T over K, stored or accumulated (fp32).
 struct ProdParams {
@@ -620,39 +651,68 @@ void prod_kernel(ProdParams a) {
   int tm, tn;
   grouped_tile(idx, a.TM, a.TN, kGroupBwd, tm, tn);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
-  f32x16_t acc[TL::R][TL::C];
+  typename TL::Acc acc[TL::R][TL::C];
   tile_mainloop<T, TL>(acc, reinterpret_cast<const T*>(a.A) + m0 * a.lda,
                        a.lda, clamp_rows(a.M - m0, kTile),
                        reinterpret_cast<const T*>(a.B) + n0 * a.ldb, a.ldb,
                        clamp_rows(a.Nc - n0, kTile), a.K, smem);
+  // The tile leaves through LDS one band of 64 rows (one row of waves) at a
+  // time: those waves write their accumulators into the band, then every
+  // thread moves 16-byte pieces of whole rows (1 KiB per wave instruction),
+  // reading all its old values (accumulate) before its first store.
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
-  const int p = lane & 31, h = lane >> 5;
-  // Loads of the old values are all issued before any store, so they
-  // overlap instead of serialising on possible aliasing.
+  constexpr int kRowF4 = TL::TN / 4;                     // float4 per tile row
+  constexpr int kPerThread = kProdBandRows * kRowF4 / TL::kThreads;
+  static_assert(kPerThread * TL::kThreads == kProdBandRows * kRowF4,
+                "whole float4 pieces per thread");
+#pragma unroll 1
+  for (int band = 0; band < TL::WM; ++band) {
+    if (wm == band) {
 #pragma unroll
-  for (int jj = 0; jj < TL::C; ++jj) {
-    const int64_t col = n0 + wn * TL::kWaveCols + jj * 32 + p;
-    const bool cok = col < a.Nc;
+      for (int i = 0; i < TL::R; ++i)
 #pragma unroll
-    for (int i = 0; i < TL::R; ++i) {
-      float old[16];
+        for (int jj = 0; jj < TL::C; ++jj) {
+          const int col = wn * TL::kWaveCols + TL::col(jj, lane);
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int64_t row = m0 + wm * TL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        old[rr] = (a.accumulate && cok && row < a.M)
-                      ? __builtin_nontemporal_load(a.out + row * a.ldo + col)
-                      : 0.f;
-      }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int64_t row = m0 + wm * TL::kWaveRows + i * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        if (cok && row < a.M)
-          __builtin_nontemporal_store(acc[i][jj][rr] + old[rr],
-                                      a.out + row * a.ldo + col);
-      }
+          for (int rr = 0; rr < TL::kAccRegs; ++rr) {
+            const int row = TL::row_base(i, rr >> 2, lane) + (rr & 3);
+            *reinterpret_cast<float*>(smem + row * kProdPitch + col * 4) =
+                acc[i][jj][rr];
+          }
+        }
     }
+    lds_barrier();
+    f32x4_t v[kPerThread];
+    bool ok[kPerThread];
+    int64_t at[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int id = tid + k * TL::kThreads;
+      const int row = id / kRowF4, c4 = id % kRowF4;
+      const int64_t grow = m0 + band * kProdBandRows + row;
+      const int64_t gcol = n0 + c4 * 4;
+      // Nc is a multiple of 4, so a piece is wholly inside or outside
+      ok[k] = grow < a.M && gcol < a.Nc;
+      at[k] = grow * a.ldo + gcol;
+      v[k] = *reinterpret_cast<const f32x4_t*>(smem + row * kProdPitch + c4 * 16);
+    }
+    if (a.accumulate) {
+      f32x4_t old[kPerThread];
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k)
+        old[k] = ok[k] ? __builtin_nontemporal_load(
+                             reinterpret_cast<const f32x4_t*>(a.out + at[k]))
+                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) v[k] += old[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+      if (ok[k])
+        __builtin_nontemporal_store(v[k], reinterpret_cast<f32x4_t*>(a.out + at[k]));
+    lds_barrier();
   }
 }
 
