@@ -664,6 +664,7 @@ void prod_kernel(ProdParams a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   constexpr int kRowF4 = TL::TN / 4;                     // float4 per tile row
+  static_assert(kRowF4 == 64, "one tile row per wave instruction");
   constexpr int kPerThread = kProdBandRows * kRowF4 / TL::kThreads;
   static_assert(kPerThread * TL::kThreads == kProdBandRows * kRowF4,
                 "whole float4 pieces per thread");
@@ -690,7 +691,10 @@ void prod_kernel(ProdParams a) {
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
       const int id = tid + k * TL::kThreads;
-      const int row = id / kRowF4, c4 = id % kRowF4;
+      // lanes 32..63 take the row's 16-byte pieces with 128-byte halves
+      // swapped, so lanes l and l + 32 (served in one LDS cycle) read
+      // different banks; the wave still covers one whole row
+      const int row = id / kRowF4, c4 = (id % kRowF4) ^ (((id >> 5) & 1) << 3);
       const int64_t grow = m0 + band * kProdBandRows + row;
       const int64_t gcol = n0 + c4 * 4;
       // Nc is a multiple of 4, so a piece is wholly inside or outside
