@@ -269,3 +269,22 @@ def test_bench_refuses_several_gpus():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("defines", [["-DVPCE_MFMA_BLOCK=32"],
+                                     ["-DVPCE_PROD_RING_RB=64",
+                                      "-DVPCE_PROD_RING_NST=4"]])
+def test_engine_build_options_compile(tmp_path, defines):
+    """The engine's build options (32 x 32 MFMA blocks; a deeper ring of
+    64-byte slabs for the products) still compile for gfx950; the default
+    build is what build() makes and the GPU tests run."""
+    from vocabulary_projection_cross_amd import build as B
+    if not os.path.exists(B.HIPCC):
+        pytest.skip("hipcc is not installed")
+    src = os.path.join(B.CSRC, "vpce.hip")
+    out = tmp_path / "vpce.o"
+    import subprocess
+    r = subprocess.run([B.HIPCC, *B.HIP_FLAGS, *defines, "-I", B.INCLUDE,
+                        "-I", B.CSRC, "--cuda-device-only", "-c", src,
+                        "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]

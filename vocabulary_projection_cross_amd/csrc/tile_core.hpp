@@ -15,9 +15,8 @@
 // (128 B x 2 stages by default), copied global -> LDS by buffer loads that
 // write LDS directly, NST - 1 stages ahead of the MFMAs. Within a row the
 // 16-byte chunk index is XOR-swizzled by row bits, so the MFMA fragment reads
-// (consecutive rows, same chunk) hit distinct banks whether the LDS serves 8
-// or 16 lanes of a 128-bit read per cycle; the copies write 1 KiB contiguous
-// blocks.
+// hit 64 distinct banks in every LDS cycle (see Ring); the copies write 1 KiB
+// contiguous blocks.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -259,8 +258,9 @@ __device__ __forceinline__ void copy16_to_lds(uint32_t lds_addr,
 }
 
 // A byte offset that every buffer resource here rejects (loads read zero).
-// Resources span less than 2^31 bytes and a block offset (fewer than 64 rows
-// of at most 2^22 bytes) added to it stays below 2^32, so it stays rejected.
+// Resources span less than 2^31 bytes and a block offset (at most 256 rows of
+// at most 2^22 bytes: under 2^30) added to it stays below 2^32, so it stays
+// rejected.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
@@ -322,8 +322,11 @@ __device__ __forceinline__ void tile_mainloop_ring(
   // l % kChunks. The swizzle depends on row bits 0..4 only and W blocks span
   // a multiple of 32 rows, so every block of a wave has the same swizzle
   // pattern, that of the wave's first block: one chunk per lane.
-  static_assert(L::kWaves * P::kBlockRows % 32 == 0,
-                "a wave's blocks share their swizzle");
+  static_assert((L::kWaves * P::kBlockRows) % 32 == 0 &&
+                    (P::kBlocksA - 1) * L::kWaves * P::kBlockRows <= 256 &&
+                    (P::kBlocksB - 1) * L::kWaves * P::kBlockRows <= 256,
+                "a wave's blocks share their swizzle; block offsets stay "
+                "within 256 rows (see kOutOfRange)");
   constexpr int W = L::kWaves;
   const int crow = lane / P::kChunks;
   const int slot = lane % P::kChunks;
