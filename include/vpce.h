@@ -35,8 +35,8 @@
  *    Concurrent calls must use distinct workspaces.
  *  - Requirements: 0 <= N <= 2000000, 1 <= d <= 1000000, V >= 1,
  *    1 <= R <= V, V < 2^31, d a multiple of 8 (VPCE_BF16) or 4 (VPCE_F32),
- *    H and W 16-byte aligned,
- *    every other pointer 4-byte aligned (labels 8, workspace 256).
+ *    H, W, dH and dW 16-byte aligned (a shard's rows of W or dW then are
+ *    too), every other pointer 4-byte aligned (labels 8, workspace 256).
  */
 #ifndef VPCE_H
 #define VPCE_H

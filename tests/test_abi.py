@@ -92,6 +92,13 @@ def test_argument_errors_before_launch(lib):
     st = lib.vpce_backward(A, A, A, A, None, 4, 16, 10, 2, -100, 0, A, A, A,
                            16, None)
     assert st == 5
+    # dH and dW take 16-byte vector stores: 4-byte alignment is not enough
+    st = lib.vpce_backward(A, A, A, A, None, 4, 16, 10, 2, -100, 0, A + 4, A,
+                           A, 1 << 20, None)
+    assert st == 4
+    st = lib.vpce_backward(A, A, A, A, None, 4, 16, 10, 2, -100, 0, A, A + 8,
+                           A, 1 << 20, None)
+    assert st == 4
 
 
 def test_device_code_hash_reads_the_built_library():
@@ -219,6 +226,7 @@ def test_shard_calls_reject_bad_arguments(lib):
     assert bwd(vb=6) == 2
     assert bwd(tot=None) == 1
     assert bwd(dW=None) == 1
+    assert bwd(dW=A + 4) == 4
     assert bwd(wsb=64) == 5
     mode, act, wts = ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
     assert lib.vpce_ring_mode(4, 12, 10, 1, 0, ctypes.byref(mode),

@@ -1040,7 +1040,7 @@ int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
   if (N > 0 && (!H || !labels || !lse || !dH)) return VPCE_ERR_NULL;
   if ((H && !aligned(H, 16)) || !aligned(W, 16) || (labels && !aligned(labels, 8)) ||
       (lse && !aligned(lse, 4)) || (dloss && !aligned(dloss, 4)) ||
-      (dH && !aligned(dH, 4)) || !aligned(dW, 4) || !aligned(workspace, kAlign))
+      (dH && !aligned(dH, 16)) || !aligned(dW, 16) || !aligned(workspace, kAlign))
     return VPCE_ERR_ALIGN;
   const int64_t C = widest_chunk(N, d, V, R, dtype, workspace_bytes, false);
   if (C == 0) return VPCE_ERR_WORKSPACE;
@@ -1144,7 +1144,7 @@ int32_t vpce_shard_backward(const void* H, const void* W_shard,
   if ((H && !aligned(H, 16)) || !aligned(W_shard, 16) ||
       (labels && !aligned(labels, 8)) || (lse && !aligned(lse, 4)) ||
       !aligned(totals, 8) || (dloss && !aligned(dloss, 4)) ||
-      (dH && !aligned(dH, 4)) || !aligned(dW_shard, 4) ||
+      (dH && !aligned(dH, 16)) || !aligned(dW_shard, 16) ||
       !aligned(workspace, kAlign))
     return VPCE_ERR_ALIGN;
   const int64_t C =
