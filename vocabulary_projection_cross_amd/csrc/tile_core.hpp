@@ -539,6 +539,11 @@ __device__ __forceinline__ void tile_mainloop_ring(
 // (vocabulary on the 320 side) for the forward and the logit recompute.
 using TileLayout = Layout<256, 256, VPCE_WAVES_M, 2, VPCE_MFMA_BLOCK,
                           VPCE_PROD_RING_RB, VPCE_PROD_RING_NST>;
+// 128 x 256 tiles (32 x 128 per wave) for products whose 256 x 256 grid would
+// leave compute units idle: twice the tiles, at 50% more copied bytes per
+// flop.
+using HalfTileLayout = Layout<128, 256, 4, 2, VPCE_MFMA_BLOCK,
+                              VPCE_PROD_RING_RB, VPCE_PROD_RING_NST>;
 using WideLayout = Layout<256, VPCE_WIDE_COLS, 4, 2>;
 template <typename L>
 using RingOf = Ring<L::RB, L::NST, L::TM, L::TN, L::kWaves>;

@@ -54,13 +54,14 @@ constexpr int kGroupRec = 4;  // the backward's logit recompute
 constexpr int kLabIgnored = -2;   // label slot codes in LDS
 constexpr int kLabInvalid = -1;
 using TL = TileLayout;  // dW and dH products
+using HL = HalfTileLayout;  // the products where 256 x 256 tiles are few
 using FL = WideLayout;  // forward and logit recompute: 256 tokens x FL::TN
 constexpr int kTile = 256;  // token tile of every kernel; product tile side
-static_assert(FL::TM == kTile && TL::TM == kTile && TL::TN == kTile,
+static_assert(FL::TM == kTile && TL::TM == kTile && TL::TN == kTile &&
+                  HL::TN == kTile,
               "token tiles and product tiles are 256 rows");
 static_assert(FL::WN == 2, "forward row merge pairs two waves per row");
 constexpr int kFwdWaves = FL::kWaves / 4;  // waves per SIMD
-constexpr int kProdWaves = TL::kWaves / 4;
 
 struct Shards {
   int64_t V;
@@ -622,12 +623,16 @@ void recompute_g_kernel(GParams a) {
   }
 }
 
-// Output staging of the products: a band of 64 tile rows in fp32, rows padded
-// by 16 bytes (the lanes of one accumulator write hit 64 distinct banks).
-constexpr int kProdBandRows = TL::kWaveRows;
-constexpr int kProdPitch = TL::TN * 4 + 16;
-static_assert(kProdBandRows * kProdPitch <= RingOf<TL>::kBytes,
-              "a band fits the operand ring");
+// Output staging of the products: a band of one row of waves' tile rows in
+// fp32, rows padded by 16 bytes (the lanes of one accumulator write hit 64
+// distinct banks).
+template <typename L>
+struct ProdStage {
+  static constexpr int kBandRows = L::kWaveRows;
+  static constexpr int kPitch = L::TN * 4 + 16;
+  static_assert(kBandRows * kPitch <= RingOf<L>::kBytes,
+                "a band fits the operand ring");
+};
 
 // out[M x Nc] (row stride ldo) = A . B^T over K, stored or accumulated (fp32).
 struct ProdParams {
@@ -645,43 +650,45 @@ struct ProdParams {
   int group;  // grouped raster: output-row tiles per group
 };
 
-template <typename T>
-__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(kProdWaves, kProdWaves)))
+template <typename T, typename PL>
+__global__ __launch_bounds__(PL::kThreads) __attribute__((amdgpu_waves_per_eu(PL::kWaves / 4, PL::kWaves / 4)))
 void prod_kernel(ProdParams a) {
-  __shared__ __attribute__((aligned(16))) char smem[RingOf<TL>::kBytes];
+  constexpr int kProdBandRows = ProdStage<PL>::kBandRows;
+  constexpr int kProdPitch = ProdStage<PL>::kPitch;
+  __shared__ __attribute__((aligned(16))) char smem[RingOf<PL>::kBytes];
   const int total = a.TM * a.TN;
   const int idx = xcd_remap(blockIdx.x, total);
   int tm, tn;
   grouped_tile(idx, a.TM, a.TN, a.group, tm, tn);
-  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
-  typename TL::Acc acc[TL::R][TL::C];
-  tile_mainloop<T, TL>(acc, reinterpret_cast<const T*>(a.A) + m0 * a.lda,
-                       a.lda, clamp_rows(a.M - m0, kTile),
+  const int64_t m0 = (int64_t)tm * PL::TM, n0 = (int64_t)tn * PL::TN;
+  typename PL::Acc acc[PL::R][PL::C];
+  tile_mainloop<T, PL>(acc, reinterpret_cast<const T*>(a.A) + m0 * a.lda,
+                       a.lda, clamp_rows(a.M - m0, PL::TM),
                        reinterpret_cast<const T*>(a.B) + n0 * a.ldb, a.ldb,
-                       clamp_rows(a.Nc - n0, kTile), a.K, smem);
+                       clamp_rows(a.Nc - n0, PL::TN), a.K, smem);
   // The tile leaves through LDS one band of 64 rows (one row of waves) at a
   // time: those waves write their accumulators into the band, then every
   // thread moves 16-byte pieces of whole rows (1 KiB per wave instruction),
   // reading all its old values (accumulate) before its first store.
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / TL::WN, wn = wave % TL::WN;
-  constexpr int kRowF4 = TL::TN / 4;                     // float4 per tile row
+  const int wm = wave / PL::WN, wn = wave % PL::WN;
+  constexpr int kRowF4 = PL::TN / 4;                     // float4 per tile row
   static_assert(kRowF4 == 64, "one tile row per wave instruction");
-  constexpr int kPerThread = kProdBandRows * kRowF4 / TL::kThreads;
-  static_assert(kPerThread * TL::kThreads == kProdBandRows * kRowF4,
+  constexpr int kPerThread = kProdBandRows * kRowF4 / PL::kThreads;
+  static_assert(kPerThread * PL::kThreads == kProdBandRows * kRowF4,
                 "whole float4 pieces per thread");
 #pragma unroll 1
-  for (int band = 0; band < TL::WM; ++band) {
+  for (int band = 0; band < PL::WM; ++band) {
     if (wm == band) {
 #pragma unroll
-      for (int i = 0; i < TL::R; ++i)
+      for (int i = 0; i < PL::R; ++i)
 #pragma unroll
-        for (int jj = 0; jj < TL::C; ++jj) {
-          const int col = wn * TL::kWaveCols + TL::col(jj, lane);
+        for (int jj = 0; jj < PL::C; ++jj) {
+          const int col = wn * PL::kWaveCols + PL::col(jj, lane);
 #pragma unroll
-          for (int rr = 0; rr < TL::kAccRegs; ++rr) {
-            const int row = TL::row_base(i, rr >> 2, lane) + (rr & 3);
+          for (int rr = 0; rr < PL::kAccRegs; ++rr) {
+            const int row = PL::row_base(i, rr >> 2, lane) + (rr & 3);
             *reinterpret_cast<float*>(smem + row * kProdPitch + col * 4) =
                 acc[i][jj][rr];
           }
@@ -693,7 +700,7 @@ void prod_kernel(ProdParams a) {
     int64_t at[kPerThread];
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
-      const int id = tid + k * TL::kThreads;
+      const int id = tid + k * PL::kThreads;
       // lanes 32..63 take the row's 16-byte pieces with 128-byte halves
       // swapped, so lanes l and l + 32 (served in one LDS cycle) read
       // different banks; the wave still covers one whole row
@@ -857,6 +864,35 @@ int32_t run_forward(const Plan& p, const void* H, const void* W,
   return VPCE_OK;
 }
 
+// Compute units of the current device (0 if the runtime cannot say).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
+// out (+)= A . B^T over pp.M output rows and pp.TN column tiles of 256: on
+// 256 x 256 tiles, or on 128 x 256 tiles where the former would give fewer
+// tiles than the device has compute units. Sets pp.TM.
+template <typename T>
+int32_t launch_prod(ProdParams pp, int cus, hipStream_t st) {
+  const int64_t tiles = (pp.M + TL::TM - 1) / TL::TM * pp.TN;
+  if (cus > 0 && tiles < cus) {
+    pp.TM = (int)((pp.M + HL::TM - 1) / HL::TM);
+    hipLaunchKernelGGL((prod_kernel<T, HL>), dim3((unsigned)(pp.TM * pp.TN)),
+                       dim3(HL::kThreads), 0, st, pp);
+  } else {
+    pp.TM = (int)((pp.M + TL::TM - 1) / TL::TM);
+    hipLaunchKernelGGL((prod_kernel<T, TL>), dim3((unsigned)(pp.TM * pp.TN)),
+                       dim3(TL::kThreads), 0, st, pp);
+  }
+  VPCE_LAUNCH_CHECK();
+  return VPCE_OK;
+}
+
 // H^T [d][N_pad] into the workspace, zero in the padding columns.
 template <typename U>
 int32_t transpose_h(const Plan& p, const void* H, char* ws, hipStream_t st) {
@@ -888,6 +924,7 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
   void* WT = ws + p.o_WT;
   const int TD = (int)((p.d + kTile - 1) / kTile);
   bool acc_h = dH_acc;
+  const int cus = device_cus();
   for (int64_t c0 = 0; c0 < v_count; c0 += p.C) {
     const int64_t ceff = (v_count - c0) < p.C ? (v_count - c0) : p.C;
     const int64_t cpad = (ceff + 63) / 64 * 64;
@@ -910,20 +947,17 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
     }
     // dW rows of the chunk = G^T H : A = G^T [C_pad x N_pad], B = H^T
     {
-      const int TM = (int)((ceff + kTile - 1) / kTile);
       ProdParams pp{GT, p.N_pad, ceff, HT, p.N_pad, p.d, p.N_pad,
-                    dWspan + c0 * p.d, p.d, TM, TD, dW_acc ? 1 : 0, kGroupDW};
-      hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(TM * TD)), dim3(TL::kThreads), 0,
-                         st, pp);
-      VPCE_LAUNCH_CHECK();
+                    dWspan + c0 * p.d, p.d, 0, TD, dW_acc ? 1 : 0, kGroupDW};
+      const int32_t rc = launch_prod<T>(pp, cus, st);
+      if (rc != VPCE_OK) return rc;
     }
     // dH (+)= G W_chunk : A = G [N x C_pad], B = W^T chunk [d x C_pad]
     if (p.N > 0) {
-      ProdParams pp{G, cpad, p.N, WT, cpad, p.d, cpad, dH, p.d, p.T, TD,
+      ProdParams pp{G, cpad, p.N, WT, cpad, p.d, cpad, dH, p.d, 0, TD,
                     acc_h ? 1 : 0, kGroupDH};
-      hipLaunchKernelGGL(prod_kernel<T>, dim3((unsigned)(p.T * TD)), dim3(TL::kThreads), 0,
-                         st, pp);
-      VPCE_LAUNCH_CHECK();
+      const int32_t rc = launch_prod<T>(pp, cus, st);
+      if (rc != VPCE_OK) return rc;
     }
     acc_h = true;
   }
