@@ -83,6 +83,29 @@ def test_ragged_shapes(vp, case):
     full_check(vp, w, seed=7, dloss=0.75)
 
 
+def test_product_tile_switch_at_the_compute_unit_count(vp):
+    """The dW and dH products run on 128 x 256 tiles where 256 x 256 tiles
+    would be fewer than the device's compute units. With d = 2048 (8 column
+    tiles) these two shapes put dH just below and just above that count and
+    dW the other way round, so both layouts of both products meet the oracle,
+    with ragged row tails."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = cus // 8                       # 256-row tiles for cus tiles
+    cases = [
+        # N: dH just below / above;  V = 2 * chunk: dW just at / below
+        (256 * (rows - 1) - 100, 2 * (256 * rows - 192)),
+        (256 * (rows + 1) - 100, 2 * (256 * (rows - 1) - 92)),
+    ]
+    for N, V in cases:
+        dh_tiles = -(-N // 256) * 8
+        dw_tiles = -(-(V // 2) // 256) * 8
+        say(f"cus={cus} N={N} V={V}: dH tiles {dh_tiles}, dW tiles {dw_tiles}")
+        assert (dh_tiles < cus) != (dw_tiles < cus)
+        w = WL.custom(N=N, d=2048, V=V, R=2, w_std=0.02, ignore_frac=0.03,
+                      name=f"switch_n{N}_v{V}")
+        full_check(vp, w)
+
+
 def test_outlier_rows_large_logits(vp):
     w = WL.custom(1000, 256, 3000, 3, w_std=0.05, ignore_frac=0.1,
                   outlier_frac=0.05, outlier_scale=20.0, labels="zipf",
