@@ -1,9 +1,9 @@
 """HIP path vs the fp64 oracle, element by element, at sizes the oracle
 finishes in seconds: the tiny fp32 workload, the 4096-token workload, and
 ragged shapes spanning several tiles (256 tokens x 320 vocabulary columns in
-the forward and the logit recompute, 256 x 256 in the dW and dH products)
-with partial tails in every dimension; plus the degenerate cases of the
-method."""
+the forward and the logit recompute; 256 x 256 in the dW and dH products, or
+128 x 256 where 256 x 256 tiles would be fewer than the compute units) with
+partial tails in every dimension; plus the degenerate cases of the method."""
 import math
 
 import numpy as np
