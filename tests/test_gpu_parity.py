@@ -324,3 +324,24 @@ def test_planned_peak_is_the_measured_peak(vp):
     say(f"planned {plan['peak_bytes']} measured {peak}")
     assert peak == plan["peak_bytes"]
     assert math.isfinite(float(loss.item()))
+
+
+def test_seeded_random_shapes(vp):
+    """Forty shapes drawn from a fixed seed: bf16 and fp32, N up to 3000, d
+    up to 1600, V up to 6000, R from 1 to 9, none to half of the tokens
+    ignored, three logit scales and upstream gradients; every one at oracle
+    parity."""
+    rng = np.random.default_rng(12345)
+    for case in range(40):
+        dt = "bf16" if rng.random() < 0.8 else "f32"
+        mult = 8 if dt == "bf16" else 4
+        N = int(rng.integers(1, 3000))
+        d = int(rng.integers(1, 200)) * mult
+        R = int(rng.integers(1, 10))
+        V = int(rng.integers(R, 6000))
+        ign = float(rng.choice([0.0, 0.05, 0.5]))
+        w_std = float(rng.choice([0.02, 0.2, 3.0 / d ** 0.5]))
+        dloss = float(rng.choice([1.0, 0.37, 2.5]))
+        w = WL.custom(N=N, d=d, V=V, R=R, dtype=dt, w_std=w_std,
+                      ignore_frac=ign, name=f"random{case}")
+        full_check(vp, w, seed=case, dloss=dloss)
