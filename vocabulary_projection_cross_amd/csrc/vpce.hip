@@ -429,6 +429,47 @@ __global__ __launch_bounds__(256) void transpose_kernel(
   }
 }
 
+// The same for 16-bit elements with 16-byte accesses: a 64 x 64 tile is read
+// as 8-element row pieces (cols a multiple of 8, rows of src 16-byte
+// aligned), and each thread gathers 8 elements down a column of the tile
+// into one 16-byte store (dst_cols and ld_dst multiples of 64, dst 16-byte
+// aligned). Tile rows are padded to 68 elements (8-byte aligned).
+__global__ __launch_bounds__(256) void transpose16_kernel(
+    const uint16_t* __restrict__ src, int64_t ld_src, int64_t rows,
+    int64_t cols, uint16_t* __restrict__ dst, int64_t ld_dst,
+    int64_t dst_cols) {
+  constexpr int kPitch = 68;
+  __shared__ __attribute__((aligned(16))) uint16_t t[64 * kPitch];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  const int piece = tid & 7;  // 8-element piece of a row
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int row = (tid >> 3) + 32 * pass;
+    const int64_t r = r0 + row, c = c0 + piece * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < rows && c < cols)
+      v = *reinterpret_cast<const u32x4_t*>(src + r * ld_src + c);
+    u32x2_t* q = reinterpret_cast<u32x2_t*>(t + row * kPitch + piece * 8);
+    q[0] = u32x2_t{v[0], v[1]};
+    q[1] = u32x2_t{v[2], v[3]};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int col = (tid >> 3) + 32 * pass;  // row of dst
+    const int64_t c = c0 + col, r = r0 + piece * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)t[(piece * 8 + 2 * e) * kPitch + col] |
+             ((uint32_t)t[(piece * 8 + 2 * e + 1) * kPitch + col] << 16);
+    if (c < cols && r < dst_cols)
+      *reinterpret_cast<u32x4_t*>(dst + c * ld_dst + r) =
+          u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
 // The bf16 G tile leaves through LDS one wave column (FL::kWaveCols chunk
 // columns, the waves with one wn) at a time. Transposed: each chunk column
 // holds 256 tokens, padded by 16 bytes so that the lanes writing 32 different
@@ -898,9 +939,14 @@ template <typename U>
 int32_t transpose_h(const Plan& p, const void* H, char* ws, hipStream_t st) {
   if (p.N_pad > 0) {
     dim3 g((unsigned)((p.N_pad + 63) / 64), (unsigned)((p.d + 63) / 64));
-    hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st,
-                       reinterpret_cast<const U*>(H), p.d, p.N, p.d,
-                       reinterpret_cast<U*>(ws + p.o_HT), p.N_pad, p.N_pad);
+    if constexpr (sizeof(U) == 2)
+      hipLaunchKernelGGL(transpose16_kernel, g, dim3(256), 0, st,
+                         reinterpret_cast<const U*>(H), p.d, p.N, p.d,
+                         reinterpret_cast<U*>(ws + p.o_HT), p.N_pad, p.N_pad);
+    else
+      hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st,
+                         reinterpret_cast<const U*>(H), p.d, p.N, p.d,
+                         reinterpret_cast<U*>(ws + p.o_HT), p.N_pad, p.N_pad);
     VPCE_LAUNCH_CHECK();
   }
   return VPCE_OK;
@@ -933,8 +979,12 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
     // W^T chunk [d][C_pad], zero in the padding columns
     {
       dim3 g((unsigned)((cpad + 63) / 64), (unsigned)((p.d + 63) / 64));
-      hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st, Wc, p.d, ceff,
-                         p.d, reinterpret_cast<U*>(WT), cpad, cpad);
+      if constexpr (sizeof(U) == 2)
+        hipLaunchKernelGGL(transpose16_kernel, g, dim3(256), 0, st, Wc, p.d,
+                           ceff, p.d, reinterpret_cast<U*>(WT), cpad, cpad);
+      else
+        hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st, Wc, p.d,
+                           ceff, p.d, reinterpret_cast<U*>(WT), cpad, cpad);
       VPCE_LAUNCH_CHECK();
     }
     const int CT = (int)((cpad + FL::TN - 1) / FL::TN);
