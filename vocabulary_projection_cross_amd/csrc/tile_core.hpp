@@ -600,6 +600,22 @@ __device__ __forceinline__ float half_xor(float v) {
       float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), pattern));
 }
 
+// Exchange within each 16-lane DPP row with a partner whose lane index differs
+// from this lane's in bit log2(MASK): p ^ 1 and p ^ 2 (quad permutations),
+// the half-row mirror 7 - p (bit 2) and the row mirror 15 - p (bit 3).
+template <int MASK>
+__device__ __forceinline__ float row_partner(float v) {
+  constexpr int ctrl = MASK == 1   ? 0xB1    // quad_perm [1, 0, 3, 2]
+                       : MASK == 2 ? 0x4E    // quad_perm [2, 3, 0, 1]
+                       : MASK == 4 ? 0x141   // row_half_mirror
+                                   : 0x140;  // row_mirror
+  static_assert(MASK == 1 || MASK == 2 || MASK == 4 || MASK == 8,
+                "partner bit");
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF,
+                                      0xF, false));
+}
+
 // Combine two (max, sum-exp) states kept in base-2 units: the result
 // describes the union of both sets. Empty states are (-inf, 0).
 __device__ __forceinline__ void ms_merge(float& m, float& s, float m2,

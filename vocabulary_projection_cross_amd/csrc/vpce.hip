@@ -213,15 +213,19 @@ void fwd_lse_kernel(FwdParams a) {
           }
         }
       }
-      // reduce-scatter the 16 row values across the lanes that share them
-#define VPCE_RS_STEP(MASK, HALF)                                        \
+      // reduce-scatter the 16 row values across the lanes that share them:
+      // at each step a lane keeps the half of its values selected by one bit
+      // of its lane index and merges in its partner's copy of that half (the
+      // partner differs in that bit; MB = 32: XOR partner in the 32-lane
+      // half, ds_swizzle; MB = 16: a DPP partner in the 16-lane row)
+#define VPCE_RS_STEP(XCHG, MASK, HALF)                                  \
       {                                                                 \
         const bool upper = (p & (MASK)) != 0;                           \
         _Pragma("unroll") for (int k = 0; k < (HALF); ++k) {            \
           const float mk = upper ? ml[k + (HALF)] : ml[k];              \
           const float sk = upper ? sl[k + (HALF)] : sl[k];              \
-          const float mo = half_xor<MASK>(upper ? ml[k] : ml[k + (HALF)]); \
-          const float so = half_xor<MASK>(upper ? sl[k] : sl[k + (HALF)]); \
+          const float mo = XCHG<MASK>(upper ? ml[k] : ml[k + (HALF)]);  \
+          const float so = XCHG<MASK>(upper ? sl[k] : sl[k + (HALF)]);  \
           float m = mk, s = sk;                                         \
           ms_merge(m, s, mo, so);                                       \
           ml[k] = m;                                                    \
@@ -229,18 +233,18 @@ void fwd_lse_kernel(FwdParams a) {
         }                                                               \
       }
       if constexpr (MB == 32) {
-        VPCE_RS_STEP(16, 8)
-        VPCE_RS_STEP(8, 4)
-        VPCE_RS_STEP(4, 2)
-        VPCE_RS_STEP(2, 1)
+        VPCE_RS_STEP(half_xor, 16, 8)
+        VPCE_RS_STEP(half_xor, 8, 4)
+        VPCE_RS_STEP(half_xor, 4, 2)
+        VPCE_RS_STEP(half_xor, 2, 1)
         const float mo = half_xor<1>(ml[0]);
         const float so = half_xor<1>(sl[0]);
         ms_merge(ml[0], sl[0], mo, so);
       } else {
-        VPCE_RS_STEP(8, 8)
-        VPCE_RS_STEP(4, 4)
-        VPCE_RS_STEP(2, 2)
-        VPCE_RS_STEP(1, 1)
+        VPCE_RS_STEP(row_partner, 8, 8)
+        VPCE_RS_STEP(row_partner, 4, 4)
+        VPCE_RS_STEP(row_partner, 2, 2)
+        VPCE_RS_STEP(row_partner, 1, 1)
       }
 #undef VPCE_RS_STEP
       ms_merge(run_m[u], run_s[u], ml[0], sl[0]);
