@@ -1,13 +1,16 @@
-"""The autograd wrapper against the direct C-ABI calls it is built from, and
-under activation-checkpoint recompute: the loss and every gradient must be
-the same values, and the tensors saved for the backward must be H, W, the
-labels and lse [N] only (no slice of the N x V logits)."""
+"""The autograd wrapper against the fp64 oracle (plain and under activation
+checkpoint recompute) and against the direct C-ABI calls it is built from:
+the loss and every gradient must match the oracle within the parity
+tolerances and equal the direct calls, and the tensors saved for the backward
+must be H, W, the labels and lse [N] only (no slice of the N x V logits)."""
 import numpy as np
 import pytest
 import torch
 from torch.utils.checkpoint import checkpoint
 
+import oracle
 import workloads as WL
+from oracle import compare as C
 from tests.gpu_common import require_gpu, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -22,6 +25,94 @@ def _inputs(N, d, V, R, dtype, seed=0):
     w = WL.Workload(f"ag_{N}x{d}x{V}x{R}_{dtype}", N, d, V, R, dtype,
                     w_std=0.05, labels="uniform", ignore_frac=0.05)
     return to_device(WL.make_inputs(w, seed))
+
+
+def _seeded(N, d, V, R, dtype, seed=0):
+    w = WL.Workload(f"ag_{N}x{d}x{V}x{R}_{dtype}", N, d, V, R, dtype,
+                    w_std=0.05, labels="uniform", ignore_frac=0.05)
+    return WL.make_inputs(w, seed)
+
+
+def _f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,dloss", [("f32", 1.0), ("bf16", 1.0),
+                                         ("f32", 3.0), ("bf16", -0.5)])
+def test_autograd_gradients_match_the_oracle(vp, dtype, dloss):
+    """loss.backward() through the wrapper: the loss against the oracle's
+    mean loss, H.grad and W.grad (cast by autograd to the input dtype)
+    against oracle.backward on the same values."""
+    from vocabulary_projection_cross_amd.autograd import cross_entropy
+    N, d, V, R = 300, 136, 1000, 3
+    say(f"case autograd vs oracle N={N} d={d} V={V} R={R} {dtype} "
+        f"dloss={dloss}")
+    inp = _seeded(N, d, V, R, dtype, seed=21)
+    H0, W0, lab = to_device(inp)
+    H = H0.clone().requires_grad_(True)
+    W = W0.clone().requires_grad_(True)
+    loss = cross_entropy(H, W, lab, R)
+    (dloss * loss).backward()
+    torch.cuda.synchronize()
+    Hf, Wf = inp.H_f64(), inp.W_f64()
+    rloss, _ = oracle.forward(Hf, Wf, inp.labels)
+    rdH, rdW = oracle.backward(Hf, Wf, inp.labels, dloss=dloss)
+    e_loss = C.loss_rel_err(float(loss.item()), rloss)
+    okH, eH = C.grad_ok(_f64(H.grad), rdH)
+    okW, eW = C.grad_ok(_f64(W.grad), rdW)
+    say(C.report("autograd", loss=e_loss, dH_maxabs=eH[0], dH_ref=eH[1],
+                 dH_cos=eH[2], dW_maxabs=eW[0], dW_ref=eW[1], dW_cos=eW[2]))
+    assert H.grad.dtype == H.dtype and W.grad.dtype == W.dtype
+    assert e_loss <= C.LOSS_REL
+    assert okH, eH
+    assert okW, eW
+
+
+def test_checkpointed_gradients_match_the_oracle(vp):
+    """A block H = bf16(x A) followed by the loss, run under
+    torch.utils.checkpoint: W.grad against the oracle's dW on the block's H,
+    and x.grad, A.grad against the chain rule through the oracle's dH
+    (x.grad = dH A^T, A.grad = x^T dH, in fp64 on the host)."""
+    from vocabulary_projection_cross_amd.autograd import cross_entropy
+    N, d0, d, V, R = 1024, 64, 256, 4000, 4
+    say(f"case autograd checkpoint vs oracle N={N} d0={d0} d={d} V={V} R={R}")
+    g = torch.Generator(device="cuda").manual_seed(13)
+    x0 = torch.randn((N, d0), device="cuda", generator=g)
+    A0 = torch.randn((d0, d), device="cuda", generator=g) / d0 ** 0.5
+    W0 = (torch.randn((V, d), device="cuda", generator=g) * 0.1).to(
+        torch.bfloat16)
+    lab = torch.randint(0, V, (N,), device="cuda", generator=g)
+    lab[::13] = -100
+
+    def block(x, A, W):
+        H = (x @ A).to(torch.bfloat16)
+        return cross_entropy(H, W, lab, R)
+
+    x = x0.clone().requires_grad_(True)
+    A = A0.clone().requires_grad_(True)
+    W = W0.clone().requires_grad_(True)
+    loss = checkpoint(block, x, A, W, use_reentrant=False)
+    loss.backward()
+    torch.cuda.synchronize()
+    with torch.no_grad():
+        Hb = (x0 @ A0).to(torch.bfloat16)
+    Hf, Wf, y = _f64(Hb), _f64(W0), lab.cpu().numpy()
+    rloss, _ = oracle.forward(Hf, Wf, y)
+    rdH, rdW = oracle.backward(Hf, Wf, y)
+    rgx = rdH @ _f64(A0).T
+    rgA = _f64(x0).T @ rdH
+    e_loss = C.loss_rel_err(float(loss.item()), rloss)
+    oks = {}
+    for name, got, ref in (("W", W.grad, rdW), ("x", x.grad, rgx),
+                           ("A", A.grad, rgA)):
+        oks[name] = C.grad_ok(_f64(got), ref)
+    say(C.report("checkpoint", loss=e_loss,
+                 **{f"{k}_cos": v[1][2] for k, v in oks.items()},
+                 **{f"{k}_maxabs_over_ref": v[1][0] / v[1][1]
+                    for k, v in oks.items()}))
+    assert e_loss <= C.LOSS_REL
+    for name, (ok, e) in oks.items():
+        assert ok, (name, e)
 
 
 def _direct(vp, H, W, lab, R, dloss=None):

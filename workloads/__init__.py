@@ -201,3 +201,18 @@ def make_inputs(w: Workload, seed: int = 0) -> Inputs:
     W = _normal_matrix(rW, w.V, w.d, w.w_std, bf16)
     lab = make_labels(w, rLab, rPerm, rIgn)
     return Inputs(w, H, W, lab, outl)
+
+
+def fingerprint(inp: Inputs, stride: int = 997) -> str:
+    """sha256 over the shapes, every ``stride``-th row of H and W (from row
+    0), the labels and the outlier rows: identifies a seeded input set, so
+    that values stored from one generation are used only with the same
+    inputs."""
+    import hashlib
+    w = inp.workload
+    h = hashlib.sha256()
+    h.update(repr((w.N, w.d, w.V, w.dtype)).encode())
+    for a in (inp.H[::stride], inp.W[::stride], inp.labels,
+              inp.outlier_rows):
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
