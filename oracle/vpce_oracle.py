@@ -6,8 +6,9 @@ benchmark's CPU-baseline leg, never by the HIP library. numpy only.
 
 Source: "Flattening Every Memory Peak in Long-Context Mixture-of-Experts
 Training" (arXiv 2609.14306), section 3.2 "Ring-DTP" and its Figure 3; the
-abstract ("the loss and gradients stay exact"); section 2 (an operator must
-return the forward values and gradients of the implementation it replaces).
+abstract (the method keeps the loss and its gradients exact); section 2 (an
+operator must give back the same forward values and gradients as the
+implementation it stands in for).
 
 The method reaches, up to rounding order, the ordinary softmax cross-entropy of
 the logits Z = H W^T. So the plain functions here (``forward``, ``backward``,
