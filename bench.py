@@ -11,17 +11,17 @@ resident in HBM. Prints ONE JSON line on stdout.
     python bench.py --copy-calibration   # plain 1 GiB device copies, for
                                          # scaling HBM traffic counters
 
-Roofline: the dominant single launch is the forward tile kernel
-(fwd_lse_kernel: 2*N*d*V MFMA flops in one launch). Its duration is measured
-with HIP events recorded on the stream the library launches on (the current
-torch stream, which the binding passes to the C ABI), bracketing each
-vpce_forward call of the timed steps; the bracket also holds three
-microsecond-scale kernels (target fill, partial merge, loss), so the figure
-slightly understates the kernel's own rate. HBM traffic per launch comes from
-rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs of this same script, scaled by
-the counters' reading for plain device copies of known size; it is stored in
-profiles/ with a hash of the kernel sources and reported only while the
-sources still match.
+Roofline: the timed steps call the library's traced variants of the forward
+and the backward, which record a HIP event pair on the library's stream (the
+current torch stream, passed to the C ABI) around every kernel launch. The
+line's roofline block is for the kernel with the most GPU time per step: its
+algorithmic flops per launch (2*N*d*V for the forward tile kernel, 2*N*d*C
+for a backward chunk of C vocabulary columns) over its mean launch duration.
+Every kernel kind's own figures are listed under roofline.kernels. HBM
+traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs
+of this same script, scaled by the counters' reading for plain device copies
+of known size; it is stored in profiles/ with a hash of the built device code
+and reported only while that code is unchanged.
 """
 from __future__ import annotations
 
@@ -71,11 +71,70 @@ def kernel_code_hash() -> str:
     raise RuntimeError(f"{path} holds no .hip_fatbin section")
 
 
-def traffic_record(workload: str):
-    """Measured HBM bytes per fwd_lse_kernel launch, if the stored counter
+KERNEL_NAMES = {"forward_tile": "fwd_lse_kernel",
+                "recompute": "recompute_g_kernel",
+                "product_dw": "prod_kernel (dW = G^T H)",
+                "product_dh": "prod_kernel (dH += G W)",
+                "transpose": "transpose16_kernel",
+                "merge": "merge_kernel", "other": "fill/loss/scale kernels"}
+
+
+def chunk_widths(w, C):
+    """Vocabulary columns of each backward chunk, in launch order: shards in
+    ring order (the first V mod R one row wider), each cut into chunks of at
+    most C columns."""
+    base, extra = divmod(w.V, w.R)
+    out = []
+    for r in range(w.R):
+        vw = base + (1 if r < extra else 0)
+        out += [min(C, vw - c0) for c0 in range(0, vw, C)]
+    return out
+
+
+def kernel_table(w, kinds_f, fev, kinds_b, bev, C):
+    """Per kernel kind: launches per step, mean duration per launch and per
+    step (HIP events around each launch, averaged over the timed steps), and
+    the algorithmic flops of its launches (2 N d V for the forward tile
+    kernel, 2 N d C per backward chunk for the recompute and each product)."""
+    widths = chunk_widths(w, C)
+    steps = len(fev)
+    table = {}
+    for kinds, evs in ((kinds_f, fev), (kinds_b, bev)):
+        chunk = {k: 0 for k in ("recompute", "product_dw", "product_dh")}
+        for i, kind in enumerate(kinds):
+            ms = sum(evs[s][2 * i].elapsed_time(evs[s][2 * i + 1])
+                     for s in range(steps)) / steps
+            if kind == "forward_tile":
+                fl = 2.0 * w.N * w.d * w.V
+            elif kind in chunk:
+                fl = 2.0 * w.N * w.d * widths[chunk[kind]]
+                chunk[kind] += 1
+            else:
+                fl = 0.0
+            t = table.setdefault(kind, {"kernel": KERNEL_NAMES[kind],
+                                        "launches_per_step": 0,
+                                        "ms_per_step": 0.0, "flops": 0.0})
+            t["launches_per_step"] += 1
+            t["ms_per_step"] += ms
+            t["flops"] += fl
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    for t in table.values():
+        n = t["launches_per_step"]
+        t["launch_ms"] = t["ms_per_step"] / n
+        t["flops_per_launch"] = t.pop("flops") / n
+        if t["flops_per_launch"] > 0:
+            tf = t["flops_per_launch"] / (t["launch_ms"] * 1e-3) / 1e12
+            t["tflops"] = tf
+            t["frac"] = tf / peak
+    return table
+
+
+def traffic_record(workload: str, kernel: str):
+    """Measured HBM bytes per launch of `kernel`, if the stored counter
     summary was taken from the device code built now."""
+    stem = kernel.split(" ")[0]
     path = os.path.join(ROOT, "profiles",
-                        f"fwd_lse_kernel_traffic_{workload}.json")
+                        f"{stem}_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -258,13 +317,31 @@ def main():
     torch.cuda.synchronize()
     out = None
 
-    # the binding launches on torch's current stream; record there
+    # The binding launches on torch's current stream; every event is
+    # recorded there. Each timed step runs the traced calls, which bracket
+    # every kernel launch with an event pair, so per-kernel durations come
+    # from the timed steps themselves.
     stream = torch.cuda.current_stream(dev)
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for e in evs:          # torch creates the event on its first record
+            e.record(stream)
+        return evs
+
+    _, lse0, _, n_fwd = vp.forward_traced(H, W, lab, w.R, [], workspace=ws)
+    _, _, _, n_bwd = vp.backward_traced(H, W, lab, lse0, dloss, w.R, [],
+                                        workspace=ws)
+    del lse0
+    fev = [new_events(n_fwd) for _ in range(args.steps)]
+    bev = [new_events(n_bwd) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
+    kinds_f = kinds_b = None
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     with ClockSampler() as clock:
@@ -272,9 +349,11 @@ def main():
         t_all0.record(stream)
         for k in range(args.steps):
             ev[k][0].record(stream)
-            loss, lse = vp.forward(H, W, lab, w.R, workspace=ws)
+            loss, lse, kinds_f, _ = vp.forward_traced(H, W, lab, w.R, fev[k],
+                                                      workspace=ws)
             ev[k][1].record(stream)
-            dH, dW = vp.backward(H, W, lab, lse, dloss, w.R, workspace=ws)
+            dH, dW, kinds_b, _ = vp.backward_traced(H, W, lab, lse, dloss,
+                                                    w.R, bev[k], workspace=ws)
             ev[k][2].record(stream)
         t_all1.record(stream)
         torch.cuda.synchronize()
@@ -282,6 +361,9 @@ def main():
     total_ms = t_all0.elapsed_time(t_all1)
     fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
     bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
+    kernels = kernel_table(w, kinds_f, fev, kinds_b, bev,
+                           vp.plan(w.N, w.d, w.V, w.R, 1 << 62,
+                                   H.dtype)["chunk_cols"])
     out_bytes = sum(t.numel() * t.element_size() for t in (loss, lse, dH, dW))
     # peak device bytes of one step, the previous outputs released
     del loss, lse, dH, dW
@@ -296,10 +378,11 @@ def main():
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     peak_tf = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    fwd_avg = float(np.mean(fwd_ms))
-    fwd_flops = 2.0 * w.N * w.d * w.V
-    fwd_tf = fwd_flops / (fwd_avg * 1e-3) / 1e12
-    trec = traffic_record(w.name)
+    # the dominant kernel: the most GPU time per step
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dom]
+    dom_tf = dk["flops_per_launch"] / (dk["launch_ms"] * 1e-3) / 1e12
+    trec = traffic_record(w.name, dk["kernel"])
     traffic = None
     if trec is not None:
         traffic = int(trec["hbm_bytes_per_launch"])
@@ -323,7 +406,7 @@ def main():
                    "R": w.R, "global_batch": w.N, "parallelism": "none"},
         "tflops": tflops,
         "pct_mfma_peak": 100.0 * tflops / peak_tf,
-        "fwd_ms": fwd_avg,
+        "fwd_ms": float(np.mean(fwd_ms)),
         "bwd_ms": float(np.mean(bwd_ms)),
         "host_wall_ms_per_step": wall_ms,
         "peak_bytes": int(peak),
@@ -337,11 +420,17 @@ def main():
         # they differ by the 4-byte upstream-gradient scalar
         "requested_peak_bytes": int(requested_peak),
         "planned_peak_bytes": planned["peak_bytes"],
-        "roofline": {"bound": "mfma", "kernel": "fwd_lse_kernel",
-                     "achieved": fwd_tf, "peak": peak_tf, "unit": "TFLOP/s",
-                     "frac": fwd_tf / peak_tf, "traffic": traffic,
-                     "flops_per_launch": fwd_flops,
-                     "launch_ms": fwd_avg,
+        "roofline": {"bound": "mfma", "kernel": dk["kernel"],
+                     "achieved": dom_tf, "peak": peak_tf, "unit": "TFLOP/s",
+                     "frac": dom_tf / peak_tf, "traffic": traffic,
+                     "flops_per_launch": dk["flops_per_launch"],
+                     "launch_ms": dk["launch_ms"],
+                     "launches_per_step": dk["launches_per_step"],
+                     "share_of_step": dk["ms_per_step"] / ms,
+                     # the whole step against the same peak, and every
+                     # kernel's own figures (HIP events around each launch)
+                     "step_frac": tflops / peak_tf,
+                     "kernels": kernels,
                      # the published peak assumes a 2400 MHz shader clock;
                      # this is the clock the chip held during the timed steps
                      "sclk_mhz_timed": clock.median(),

@@ -74,7 +74,9 @@ typedef enum {
  * depend on V: the forward keeps per-token partial states for R shards times
  * a fixed number of vocabulary splits, the backward a fixed-width chunk of
  * recomputed logit gradients. Returns 0 for arguments vpce_forward would
- * reject.
+ * reject. Sizing helper of this library: the memory it sizes stands in for
+ * the per-round logit strip of section 3.2 (see vpce_workspace_bytes_chunk),
+ * but no passage defines the call itself.
  */
 size_t vpce_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
                             int32_t dtype);
@@ -83,9 +85,9 @@ size_t vpce_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
  * As vpce_workspace_bytes, for a backward chunk of chunk_cols vocabulary
  * columns (a multiple of 256 in [256, 16384]; 0 is returned otherwise). The
  * backward chunk is the memory that stands in for the logit strip of section
- * 3.2: its gradient chunk G [N x C], G^T and the W chunk^T grow linearly
- * with C.
- * Narrower chunks cost more passes of the fp32 dH read-modify-write.
+ * 3.2: the backward's workspace is its gradient chunk G [N x C] (bf16 for
+ * bf16 inputs, fp32 for fp32), one N x C strip. Narrower chunks cost more
+ * passes of the fp32 dH read-modify-write.
  */
 size_t vpce_workspace_bytes_chunk(int64_t N, int64_t d, int64_t V, int32_t R,
                                   int32_t dtype, int64_t chunk_cols);
@@ -160,6 +162,57 @@ int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
                       int64_t d, int64_t V, int32_t R, int64_t ignore_index,
                       int32_t dtype, float* dH, float* dW, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * ---- Timed variants ---------------------------------------------------------
+ *
+ * vpce_forward_traced and vpce_backward_traced do exactly the work of
+ * vpce_forward and vpce_backward (same arguments, same results) and also
+ * record timing events around their kernel launches, so that a caller can
+ * measure each kernel's duration with hipEventElapsedTime on the stream the
+ * kernels run on. Builder utility for measurement; no passage of the paper
+ * defines it.
+ *   events        2 * max_launches hipEvent_t handles created by the caller
+ *                 (with timing enabled); events[2i] is recorded on `stream`
+ *                 right before the i-th launch and events[2i + 1] right after
+ *   max_launches  how many launches to bracket (0 is allowed: nothing is
+ *                 recorded)
+ *   kinds         out [max_launches]: vpce_kernel_kind_t of each bracketed
+ *                 launch
+ *   n_launches    out: the number of kernels the call launched (may exceed
+ *                 max_launches; the later ones are not bracketed)
+ * Argument errors are returned before anything is enqueued, as for the
+ * untimed calls (a NULL event among the first 2 * max_launches is
+ * VPCE_ERR_NULL). If an event cannot be recorded, VPCE_ERR_HIP is returned.
+ */
+typedef enum {
+  VPCE_KERNEL_FORWARD_TILE = 1, /* logit tiles + online log-sum-exp */
+  VPCE_KERNEL_MERGE = 2,        /* fold of shard/split partials, token NLL */
+  VPCE_KERNEL_RECOMPUTE = 3,    /* backward: logit recompute, G chunk */
+  VPCE_KERNEL_PRODUCT_DW = 4,   /* backward: dW rows of a chunk = G^T H */
+  VPCE_KERNEL_PRODUCT_DH = 5,   /* backward: dH += G W_chunk */
+  VPCE_KERNEL_TRANSPOSE = 6,    /* operand layout copies */
+  VPCE_KERNEL_OTHER = 7         /* fills, loss mean, gradient scale */
+} vpce_kernel_kind_t;
+
+int32_t vpce_forward_traced(const void* H, const void* W,
+                            const int64_t* labels, int64_t N, int64_t d,
+                            int64_t V, int32_t R, int64_t ignore_index,
+                            int32_t dtype, float* loss, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* events,
+                            int32_t max_launches, int32_t* kinds,
+                            int32_t* n_launches);
+
+int32_t vpce_backward_traced(const void* H, const void* W,
+                             const int64_t* labels, const float* lse,
+                             const float* dloss, int64_t N, int64_t d,
+                             int64_t V, int32_t R, int64_t ignore_index,
+                             int32_t dtype, float* dH, float* dW,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream, void* const* events,
+                             int32_t max_launches, int32_t* kinds,
+                             int32_t* n_launches);
 
 /*
  * ---- Shard-level calls: one batch meets one vocabulary shard --------------
@@ -255,7 +308,8 @@ int32_t vpce_shard_backward(const void* H, const void* W_shard,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
-/* Static, NUL-terminated description of a status code. */
+/* Static, NUL-terminated description of a status code. Library utility;
+   no passage of the paper defines it. */
 const char* vpce_status_string(int32_t status);
 
 #ifdef __cplusplus

@@ -29,7 +29,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert names == ["vpce_backward", "vpce_forward", "vpce_plan",
+    assert names == ["vpce_backward", "vpce_backward_traced", "vpce_forward",
+                     "vpce_forward_traced", "vpce_plan",
                      "vpce_ring_mode", "vpce_shard_backward",
                      "vpce_shard_fold", "vpce_state_finish",
                      "vpce_state_init", "vpce_status_string",
@@ -245,14 +246,64 @@ def test_bench_traffic_record_goes_stale_with_the_device_code(tmp_path,
     rec = {"kernel_code_hash": built, "hbm_bytes_per_launch": 123}
     prof = tmp_path / "profiles"
     prof.mkdir()
-    (prof / "fwd_lse_kernel_traffic_w.json").write_text(json.dumps(rec))
+    (prof / "prod_kernel_traffic_w.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_code_hash", lambda: built)
-    assert bench.traffic_record("w")["hbm_bytes_per_launch"] == 123
+    k = "prod_kernel (dH += G W)"
+    assert bench.traffic_record("w", k)["hbm_bytes_per_launch"] == 123
+    assert bench.traffic_record("w", "fwd_lse_kernel") is None
     rec["kernel_code_hash"] = "0" * 16
-    (prof / "fwd_lse_kernel_traffic_w.json").write_text(json.dumps(rec))
-    assert bench.traffic_record("w") is None
-    assert bench.traffic_record("missing") is None
+    (prof / "prod_kernel_traffic_w.json").write_text(json.dumps(rec))
+    assert bench.traffic_record("w", k) is None
+    assert bench.traffic_record("missing", k) is None
+
+
+def test_bench_kernel_table_from_event_pairs():
+    """Per-kernel figures of the bench line: launches per step, mean launch
+    time over the timed steps, and flops per launch from the chunk widths
+    (shards in ring order, each cut into chunks of at most C columns)."""
+    import bench
+    import workloads as WL
+
+    class Ev:
+        def __init__(self, t):
+            self.t = t
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    w = WL.custom(N=1000, d=64, V=10, R=3, name="t")   # shards 4, 3, 3
+    assert bench.chunk_widths(w, 2) == [2, 2, 2, 1, 2, 1]
+    assert bench.chunk_widths(w, 16384) == [4, 3, 3]
+    kinds_f = ["other", "forward_tile", "merge", "other"]
+    kinds_b = ["other", "transpose"] + ["transpose", "recompute",
+                                        "product_dw", "product_dh"] * 3
+
+    def evs(kinds, steps, dur):
+        out = []
+        for s in range(steps):
+            e = []
+            for i, k in enumerate(kinds):
+                e += [Ev(0.0), Ev(dur(k, i) * (1 + s))]
+            out.append(e)
+        return out
+
+    fev = evs(kinds_f, 2, lambda k, i: 4.0 if k == "forward_tile" else 0.01)
+    bev = evs(kinds_b, 2, lambda k, i: {"product_dw": 2.0,
+                                        "product_dh": 3.0}.get(k, 0.5))
+    t = bench.kernel_table(w, kinds_f, fev, kinds_b, bev, 16384)
+    # durations of step s are (1 + s) x base: the mean over 2 steps is 1.5 x
+    assert t["forward_tile"]["launches_per_step"] == 1
+    assert t["forward_tile"]["launch_ms"] == 6.0
+    assert t["forward_tile"]["flops_per_launch"] == 2.0 * 1000 * 64 * 10
+    assert t["product_dh"]["launches_per_step"] == 3
+    assert t["product_dh"]["ms_per_step"] == 13.5
+    assert t["product_dh"]["flops_per_launch"] == 2.0 * 1000 * 64 * 10 / 3
+    assert t["transpose"]["launches_per_step"] == 4
+    assert "frac" not in t["transpose"]
+    assert t["other"]["launches_per_step"] == 3
+    dom = max(t, key=lambda k: t[k]["ms_per_step"])
+    assert dom == "product_dh"
 
 
 def test_bench_clock_sampler_without_the_tool(monkeypatch):
@@ -280,12 +331,14 @@ def test_bench_refuses_several_gpus():
 
 
 @pytest.mark.parametrize("defines", [["-DVPCE_MFMA_BLOCK=32"],
-                                     ["-DVPCE_PROD_RING_RB=64",
-                                      "-DVPCE_PROD_RING_NST=4"]])
+                                     ["-DVPCE_RING_RB=64",
+                                      "-DVPCE_RING_NST=4",
+                                      "-DVPCE_WIDE_COLS=256"]])
 def test_engine_build_options_compile(tmp_path, defines):
-    """The engine's build options (32 x 32 MFMA blocks; a deeper ring of
-    64-byte slabs for the products) still compile for gfx950; the default
-    build is what build() makes and the GPU tests run."""
+    """The engine's build options for the forward and the logit recompute
+    (32 x 32 MFMA blocks; a deeper ring of 64-byte slabs on 256-column
+    tiles) still compile for gfx950; the default build is what build() makes
+    and the GPU tests run."""
     from vocabulary_projection_cross_amd import build as B
     if not os.path.exists(B.HIPCC):
         pytest.skip("hipcc is not installed")
@@ -296,3 +349,37 @@ def test_engine_build_options_compile(tmp_path, defines):
                         "-I", B.CSRC, "--cuda-device-only", "-c", src,
                         "-o", str(out)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_traced_calls_check_their_trace_arguments(lib):
+    """The timed variants refuse bad trace arguments before anything is
+    enqueued (no GPU is touched on these paths)."""
+    import ctypes
+    A = 1 << 20                       # any 256-aligned address; never read
+    n = ctypes.c_int32(0)
+    kinds = (ctypes.c_int32 * 4)()
+    evs = (ctypes.c_void_p * 8)(*([A] * 8))
+
+    def fwd(events, cap, k, used):
+        return lib.vpce_forward_traced(A, A, A, 4, 16, 10, 2, -100, 0, A, A,
+                                       A, 1 << 20, None, events, cap, k, used)
+
+    def bwd(events, cap, k, used):
+        return lib.vpce_backward_traced(A, A, A, A, None, 4, 16, 10, 2, -100,
+                                        0, A, A, A, 1 << 20, None, events,
+                                        cap, k, used)
+
+    for call in (fwd, bwd):
+        assert call(evs, -1, kinds, ctypes.byref(n)) == 2
+        assert call(None, 4, kinds, ctypes.byref(n)) == 1
+        assert call(evs, 4, None, ctypes.byref(n)) == 1
+        assert call(evs, 4, kinds, None) == 1
+        holes = (ctypes.c_void_p * 8)(*([A] * 7 + [None]))
+        assert call(holes, 4, kinds, ctypes.byref(n)) == 1
+        # argument errors of the untimed call come through unchanged
+    assert lib.vpce_forward_traced(A, A, A, 4, 12, 10, 2, -100, 0, A, A, A,
+                                   1 << 20, None, evs, 4, kinds,
+                                   ctypes.byref(n)) == 2
+    assert lib.vpce_backward_traced(A, A, A, A, None, 4, 16, 10, 2, -100, 0,
+                                    A, A, A, 64, None, evs, 4, kinds,
+                                    ctypes.byref(n)) == 5

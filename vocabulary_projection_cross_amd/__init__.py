@@ -21,6 +21,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["forward", "backward", "workspace_bytes", "plan", "ring_mode",
+           "forward_traced", "backward_traced", "KERNEL_KINDS",
            "state_init", "shard_fold", "state_finish", "shard_backward",
            "VPCEError", "library_path", "IGNORE_INDEX", "VPCE_BF16",
            "VPCE_F32", "MOVE_WEIGHTS", "MOVE_ACTIVATIONS"]
@@ -66,6 +67,15 @@ def _load():
     lib.vpce_forward.restype = i32
     lib.vpce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i32,
                                  vp, vp, vp, sz, vp]
+    for name, n_args in (("vpce_forward_traced", 14),
+                         ("vpce_backward_traced", 16)):
+        f = getattr(lib, name)
+        f.restype = i32
+        base = (lib.vpce_forward.argtypes if n_args == 14
+                else [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, vp,
+                      vp, vp, sz, vp])
+        f.argtypes = list(base) + [ctypes.POINTER(vp), i32,
+                                   ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.vpce_backward.restype = i32
     lib.vpce_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64,
                                   i32, vp, vp, vp, sz, vp]
@@ -229,6 +239,72 @@ def backward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
                                _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
     _check(st)
     return dH, dW
+
+
+# ---- timed variants (measurement) -----------------------------------------
+
+KERNEL_KINDS = {1: "forward_tile", 2: "merge", 3: "recompute",
+                4: "product_dw", 5: "product_dh", 6: "transpose", 7: "other"}
+
+
+def _trace_args(events):
+    """ctypes arguments for an event list: every event must already exist
+    (torch creates an event on its first record)."""
+    handles = [int(e.cuda_event) for e in events]
+    if len(handles) % 2 or any(h == 0 for h in handles):
+        raise VPCEError("events must be an even number of recorded "
+                        "torch.cuda.Event objects")
+    n = len(handles) // 2
+    arr = (ctypes.c_void_p * max(1, len(handles)))(*handles)
+    kinds = (ctypes.c_int32 * max(1, n))()
+    return arr, n, kinds, ctypes.c_int32(0)
+
+
+def forward_traced(H, W, labels, R, events, ignore_index=IGNORE_INDEX,
+                   workspace=None):
+    """vpce_forward_traced: forward() plus timing events around its kernel
+    launches (pair i = events[2i], events[2i+1]). Returns (loss, lse,
+    [kind of each bracketed launch], number of launches)."""
+    _validate(H, W, labels)
+    lib = _load()
+    N, d = H.shape
+    V = W.shape[0]
+    ws = _workspace(H, W, R, workspace)
+    loss = torch.empty((), dtype=torch.float32, device=H.device)
+    lse = torch.empty(N, dtype=torch.float32, device=H.device)
+    arr, n, kinds, used = _trace_args(events)
+    with torch.cuda.device(H.device):
+        st = lib.vpce_forward_traced(
+            _ptr(H), _ptr(W), _ptr(labels), N, d, V, R, ignore_index,
+            _dtype_code(H.dtype), _ptr(loss), _ptr(lse), _ptr(ws), ws.numel(),
+            _stream(H), arr, n, kinds, ctypes.byref(used))
+    _check(st)
+    return loss, lse, [KERNEL_KINDS[kinds[i]] for i in
+                       range(min(n, used.value))], int(used.value)
+
+
+def backward_traced(H, W, labels, lse, dloss, R, events,
+                    ignore_index=IGNORE_INDEX, workspace=None):
+    """vpce_backward_traced: backward() plus timing events around its kernel
+    launches. Returns (dH, dW, [kind of each bracketed launch], number of
+    launches)."""
+    _validate(H, W, labels)
+    lib = _load()
+    N, d = H.shape
+    V = W.shape[0]
+    ws = _workspace(H, W, R, workspace)
+    dH = torch.empty((N, d), dtype=torch.float32, device=H.device)
+    dW = torch.empty((V, d), dtype=torch.float32, device=H.device)
+    arr, n, kinds, used = _trace_args(events)
+    with torch.cuda.device(H.device):
+        st = lib.vpce_backward_traced(
+            _ptr(H), _ptr(W), _ptr(labels), _ptr(lse), _ptr(dloss), N, d, V,
+            R, ignore_index, _dtype_code(H.dtype), _ptr(dH), _ptr(dW),
+            _ptr(ws), ws.numel(), _stream(H), arr, n, kinds,
+            ctypes.byref(used))
+    _check(st)
+    return dH, dW, [KERNEL_KINDS[kinds[i]] for i in
+                    range(min(n, used.value))], int(used.value)
 
 
 # ---- shard-level calls: one batch meets one vocabulary shard ---------------

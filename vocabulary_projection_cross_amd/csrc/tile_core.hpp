@@ -37,9 +37,10 @@ constexpr int kLdsBytes = 160 * 1024;  // LDS of one workgroup on gfx950
 // full step (whole 128-byte lines per request, a barrier every four K-steps
 // of 32 x 32 blocks instead of two), and 4 x 2 waves ahead of 2 x 2. 64-byte
 // slabs copy 16-row blocks, which a 320-row operand does not split into over
-// 8 waves, so they build only with VPCE_WIDE_COLS=256; for the 256 x 256
-// products (VPCE_PROD_RING_RB/NST) a 3-, 4- or 5-deep ring of 64-byte slabs
-// is 4% slower than the default.
+// 8 waves, so they build only with VPCE_WIDE_COLS=256. These options shape
+// the forward and the logit recompute; the products are fixed (see
+// TileLayout). For the products, a 3-, 4- or 5-deep ring of 64-byte slabs
+// was measured 4% slower than the two-stage ring of 128-byte slabs.
 #ifndef VPCE_WAVES_M
 #define VPCE_WAVES_M 4
 #endif
@@ -48,12 +49,6 @@ constexpr int kLdsBytes = 160 * 1024;  // LDS of one workgroup on gfx950
 #endif
 #ifndef VPCE_RING_NST
 #define VPCE_RING_NST 2
-#endif
-#ifndef VPCE_PROD_RING_RB
-#define VPCE_PROD_RING_RB VPCE_RING_RB
-#endif
-#ifndef VPCE_PROD_RING_NST
-#define VPCE_PROD_RING_NST VPCE_RING_NST
 #endif
 #ifndef VPCE_WIDE_COLS
 #define VPCE_WIDE_COLS 320
@@ -139,20 +134,58 @@ struct Layout {
 // fragments); the swizzle sends either set to 64 distinct banks. (With row
 // bit 3 in place of bit 4, 16 x 16 fragment reads collide two ways and cost
 // twice the LDS cycles.)
-template <int RB, int NST, int TM, int TN, int WAVES>
+// Stage layout of a K-outer operand: in memory each row is one k (the
+// tile's TX entries of the M or N side are contiguous in it), so a stage holds
+// BK k-rows of TX entries, row k at k * kRowBytes (two rows per 1 KiB copy
+// block for bf16 tiles of 256, one for fp32). In a bf16 row k the logical
+// 32-byte segment s sits at segment s ^ f(k), f(k) = (k & 3) | ((k >> 3) & 1)
+// << 2. A transposing read (see tile_mainloop_ring) touches k-rows
+// {8h + 4e + j : j < 4} of one logical segment in each 16-lane group h; the
+// groups h = 0, 1 (and 2, 3) thus see f = j + 4 (h & 1), eight distinct
+// segments, 64 distinct banks. Measured on gfx950 with probe patterns: 306
+// bytes per clock per compute unit for such reads, against 289 for the
+// swizzled 16-byte fragment reads of K-contiguous operands (and 72 for the
+// same transposing reads without the XOR). fp32 rows are not swizzled.
+template <typename T, int TX, int RB>
+struct KOuter {
+  static constexpr int kRowBytes = TX * (int)sizeof(T);
+  // (defined for every tile width so that K-contiguous uses of Ring can name
+  // it; only kSupported shapes are ever read K-outer)
+  static constexpr int kRows = kRowBytes <= 1024 ? 1024 / kRowBytes : 1;
+  static constexpr int BK = RB / (int)sizeof(T);
+  static constexpr int kBlocks = BK / kRows;
+  static constexpr int kBytes = BK * kRowBytes;
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  // rows of 512 (bf16) or 1024 bytes (fp32): tiles of 256 entries
+  static constexpr bool kSupported = kRows * kRowBytes == 1024 &&
+                                     kBlocks * kRows == BK &&
+                                     (kRows == 1 || kRows == 2);
+  __device__ static constexpr int swz(int k) {
+    return sizeof(T) == 2 ? (k & 3) | (((k >> 3) & 1) << 2) : 0;
+  }
+};
+
+template <int RB, int NST, int TM, int TN, int WAVES, typename T = __bf16,
+          bool TA = false, bool TB = false>
 struct Ring {
   static_assert(RB == 64 || RB == 128, "row bytes per stage");
   static constexpr int kChunks = RB / 16;              // chunks per row
   static constexpr int kBlockRows = 1024 / RB;         // rows per 1 KiB copy
-  static constexpr int kBlocksA = TM / kBlockRows / WAVES;  // per wave
-  static constexpr int kBlocksB = TN / kBlockRows / WAVES;
-  static constexpr int kOperandBytesA = TM * RB;
-  static constexpr int kStageBytes = (TM + TN) * RB;
+  using KA = KOuter<T, TM, RB>;
+  using KB = KOuter<T, TN, RB>;
+  static constexpr int kBlocksA =
+      (TA ? KA::kBlocks : TM / kBlockRows) / WAVES;  // per wave
+  static constexpr int kBlocksB = (TB ? KB::kBlocks : TN / kBlockRows) / WAVES;
+  static constexpr int kOperandBytesA = TA ? KA::kBytes : TM * RB;
+  static constexpr int kOperandBytesB = TB ? KB::kBytes : TN * RB;
+  static constexpr int kStageBytes = kOperandBytesA + kOperandBytesB;
   static constexpr int kBytes = NST * kStageBytes;
   static constexpr int kCopies = kBlocksA + kBlocksB;  // per wave per stage
-  static_assert(kBlocksA * kBlockRows * WAVES == TM &&
-                    kBlocksB * kBlockRows * WAVES == TN && kBlocksA >= 1 &&
-                    kBlocksB >= 1,
+  static_assert((TA ? kBlocksA * WAVES == KA::kBlocks
+                    : kBlocksA * kBlockRows * WAVES == TM) &&
+                    (TB ? kBlocksB * WAVES == KB::kBlocks
+                        : kBlocksB * kBlockRows * WAVES == TN) &&
+                    kBlocksA >= 1 && kBlocksB >= 1,
                 "every wave copies whole blocks of both operands");
   static_assert(kBytes <= kLdsBytes, "ring exceeds the LDS");
   __device__ static constexpr int swz(int row) {
@@ -258,10 +291,13 @@ __device__ __forceinline__ void copy16_to_lds(uint32_t lds_addr,
 }
 
 // A byte offset that every buffer resource here rejects (loads read zero).
-// Resources span less than 2^31 bytes and a block offset (at most 256 rows of
-// at most 2^22 bytes: under 2^30) added to it stays below 2^32, so it stays
-// rejected.
+// Resources span less than 2^31 bytes, and a block offset added to it (at
+// most 256 rows of an operand pitch; the longest pitch is a row of an fp32
+// transposed H, 4 * N_pad bytes, which the library's token limit keeps below
+// 8.0e6, so under 2.05e9) leaves it below 2^32, so it stays rejected. The
+// library checks that bound against its shape limits at compile time.
 constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int64_t kMaxBlockOffsetRows = 256;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt_hi[15:14]); unnamed counters left at their maximum.
@@ -270,35 +306,62 @@ constexpr int waitcnt_vm_lgkm(int vm, int lgkm) {
 }
 
 // acc = A[0:TM, 0:K] . B[0:TN, 0:K]^T for the workgroup's tile; this wave's
-// sub-tile lands in acc (layout L). A, B point at the tile's first row;
-// a_rows / b_rows are the valid rows (clamped by the caller to [0, TM] and
-// [0, TN]); TM * ld * sizeof(T) and TN * ld * sizeof(T) must stay below 2^31
-// bytes and K must be a multiple of 16 bytes' worth of T (checked on the
-// host). smem must hold the ring's kBytes. Ends with every copy landed and a
-// workgroup barrier, so smem may be reused right after.
+// sub-tile lands in acc (layout L).
+//
+// Each operand is K-contiguous (the default: rows of memory are rows of the
+// tile, K runs along them) or K-outer (TA / TB: rows of memory are k, the
+// tile's entries run along them, as for the token-major G, H and W read by
+// the backward products).
+//  * K-contiguous X: X points at the tile's first row, ldx is the row pitch,
+//    x_rows the valid rows (clamped by the caller to [0, TM] or [0, TN]);
+//    TM * ldx * sizeof(T) stays below 2^31 bytes; chunks past K read zero.
+//  * K-outer X: X points at row k = 0 of the whole matrix, x_col0 is the
+//    tile's first entry in a row, ldx the row pitch (a multiple of 16 bytes),
+//    x_rows the valid k-rows: rows past it read zero. Entries past the end of
+//    a row are the next row's (they only reach outputs the caller discards);
+//    the matrix ends at row x_rows. BK * ldx * sizeof(T) stays below 2^31.
+// K must be a multiple of 16 bytes' worth of T (checked on the host). smem
+// must hold the ring's kBytes. Ends with every copy landed and a workgroup
+// barrier, so smem may be reused right after.
 //
 // Global memory is copied straight into LDS by the buffer-load-to-LDS path
 // (no register staging): per stage each wave copies kBlocksA 1 KiB blocks of
-// A and kBlocksB of B (every W-th block, W waves); lane l of a block copies
-// row l / kChunks into slot l % kChunks of that row, which holds the global
-// chunk slot ^ swz(row).
+// A and kBlocksB of B (every W-th block, W waves). K-contiguous: lane l of a
+// block copies row l / kChunks into slot l % kChunks of that row, which holds
+// the global chunk slot ^ swz(row). K-outer: lane l copies row l / 32 of the
+// block (bf16; fp32 blocks are one row) into slot l % 32 of it, which holds
+// the row's chunk with the segment XOR of KOuter; the stage's buffer
+// resource starts at its first k-row, so the 32-bit offsets stay small
+// however long K is.
 // Per stage kt (ring buffer kt % NST), each of its S K-steps runs the NG MFMA
 // groups, with the next step's fragments read at the step's start; the last
 // step starts with the workgroup barrier, after which the wave reads stage
 // kt + 1's first fragments and issues its copies of stage kt + NST into the
 // buffer stage kt leaves (see the loop for why that order is safe).
-template <typename T, typename L, int RB, int NST>
+//
+// A K-outer bf16 fragment is two transposing reads (ds_read_b64_tr_b16):
+// within each 16-lane group, lane 4a + b receives element b of the 8-byte
+// pieces addressed by lanes a, a + 4, a + 8 and a + 12. Lane a + 4j (group h)
+// addresses k-row 32 st + 8h + 4e + j, entries 4a .. 4a + 3 of the 16-entry
+// block, so lane p of the group receives k-rows 8h + 4e .. 8h + 4e + 3 of
+// entry p: read e = 0 and e = 1 together give the same 8 values of K that the
+// K-contiguous fragment holds, and the MFMAs see the same operands either
+// way. fp32 K-outer fragments are four 4-byte reads down a column.
+template <typename T, typename L, int RB, int NST, bool TA = false,
+          bool TB = false>
 __device__ __forceinline__ void tile_mainloop_ring(
     typename L::Acc (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
     int a_rows, const T* __restrict__ B, int64_t ldb, int b_rows, int64_t K,
-    char* smem) {
-  using P = Ring<RB, NST, L::TM, L::TN, L::kWaves>;
+    char* smem, int a_col0 = 0, int b_col0 = 0) {
+  using P = Ring<RB, NST, L::TM, L::TN, L::kWaves, T, TA, TB>;
   constexpr int R = L::R, C = L::C, NG = L::NG, MB = L::MB;
   constexpr int E = Chunk<T>::E;           // elements per 16-byte chunk
   constexpr int BK = RB / (int)sizeof(T);  // elements of K per stage
   constexpr int CPS = 64 / MB;             // 16-byte chunks per K-step
   constexpr int S = P::kChunks / CPS;      // K-steps per stage
   static_assert(S >= 1 && S * CPS == P::kChunks, "whole K-steps per stage");
+  static_assert(!(TA || TB) || (MB == 16 && RB == 128),
+                "K-outer operands: 16 x 16 blocks, 128-byte stages");
   constexpr int KA = P::kBlocksA, KB = P::kBlocksB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int swave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
@@ -313,40 +376,81 @@ __device__ __forceinline__ void tile_mainloop_ring(
 
   const int KT = (int)((K + BK - 1) / BK);
   if (KT <= 0) return;
-  const i32x4_t rsa = tile_rsrc_dw<T>(A, lda, a_rows);
-  const i32x4_t rsb = tile_rsrc_dw<T>(B, ldb, b_rows);
   const uint32_t lds = (uint32_t)(uintptr_t)(lds_char_t*)smem;
-
-  // copy side: wave w copies blocks w, w + W, w + 2W, ... (W waves) of each
-  // operand; lane l copies row crow = l / kChunks of a block into slot
-  // l % kChunks. The swizzle depends on row bits 0..4 only and W blocks span
-  // a multiple of 32 rows, so every block of a wave has the same swizzle
-  // pattern, that of the wave's first block: one chunk per lane.
-  static_assert((L::kWaves * P::kBlockRows) % 32 == 0 &&
-                    (P::kBlocksA - 1) * L::kWaves * P::kBlockRows <= 256 &&
-                    (P::kBlocksB - 1) * L::kWaves * P::kBlockRows <= 256,
-                "a wave's blocks share their swizzle; block offsets stay "
-                "within 256 rows (see kOutOfRange)");
   constexpr int W = L::kWaves;
+  const uint32_t pa = (uint32_t)(lda * (int64_t)sizeof(T));
+  const uint32_t pb = (uint32_t)(ldb * (int64_t)sizeof(T));
+  const uint32_t dsta = lds + (uint32_t)(swave * 1024);
+  const uint32_t dstb = lds + (uint32_t)(P::kOperandBytesA + swave * 1024);
+
+  // K-contiguous copy side: wave w copies blocks w, w + W, w + 2W, ... (W
+  // waves) of each operand; lane l copies row crow = l / kChunks of a block
+  // into slot l % kChunks. The swizzle depends on row bits 0..4 only and W
+  // blocks span a multiple of 32 rows, so every block of a wave has the same
+  // swizzle pattern, that of the wave's first block: one chunk per lane.
+  static_assert((L::kWaves * P::kBlockRows) % 32 == 0 &&
+                    (P::kBlocksA - 1) * L::kWaves * P::kBlockRows <=
+                        kMaxBlockOffsetRows &&
+                    (P::kBlocksB - 1) * L::kWaves * P::kBlockRows <=
+                        kMaxBlockOffsetRows,
+                "a wave's blocks share their swizzle; block offsets stay "
+                "within kMaxBlockOffsetRows rows (see kOutOfRange)");
   const int crow = lane / P::kChunks;
   const int slot = lane % P::kChunks;
   const int ch = slot ^ P::swz(swave * P::kBlockRows + crow);
-  const uint32_t pa = (uint32_t)(lda * (int64_t)sizeof(T));
-  const uint32_t pb = (uint32_t)(ldb * (int64_t)sizeof(T));
   const uint32_t row0 = (uint32_t)(swave * P::kBlockRows + crow);
-  const uint32_t dsta = lds + (uint32_t)(swave * 1024);
-  const uint32_t dstb = lds + (uint32_t)(P::kOperandBytesA + swave * 1024);
   // stages whose chunk lies inside K: s * BK + ch * E < K  <=>  s < klim
   const int Ki = (int)K;  // K < 2^31 (checked on the host)
   const int kl = Ki > ch * E ? (Ki - ch * E + BK - 1) / BK : 0;
   const uint32_t ra = row0 * pa + (uint32_t)(ch * 16);
   const uint32_t rb = row0 * pb + (uint32_t)(ch * 16);
-  uint32_t va, vb;
-  // lane offsets of stage s (past K -> out of range)
+
+  // K-outer copy side: lane l copies k-row k = w kRows + l / kChunksPerRow
+  // of its wave's block into slot l % kChunksPerRow, which holds the row's
+  // chunk slot ^ (2 swz(k)) (the segment XOR). The wave's later blocks are
+  // W kRows = 16 rows further on, which leaves k's bits 0, 1 and 3, and so
+  // the XOR, unchanged: one chunk per lane.
+  static_assert((!TA || P::KA::kSupported) && (!TB || P::KB::kSupported),
+                "K-outer tiles of 256 entries (bf16 or fp32)");
+  static_assert(sizeof(T) == 4 ||
+                    ((!TA || (W * P::KA::kRows) % 16 == 0) &&
+                     (!TB || (W * P::KB::kRows) % 16 == 0)),
+                "a wave's K-outer blocks share their XOR pattern");
+  auto kouter_lane = [&](auto ko, uint32_t pitch) -> uint32_t {
+    using KO = decltype(ko);
+    const int k = swave * KO::kRows + lane / KO::kChunksPerRow;
+    const int c = (lane % KO::kChunksPerRow) ^ (2 * KO::swz(k));
+    return (uint32_t)k * pitch + (uint32_t)(c * 16);
+  };
+  const uint32_t ta_lane = TA ? kouter_lane(typename P::KA{}, pa) : 0u;
+  const uint32_t tb_lane = TB ? kouter_lane(typename P::KB{}, pb) : 0u;
+  // bytes of a K-outer operand readable from its tile start (k-row 0, entry
+  // x_col0): the valid k-rows, less the part of the last row before x_col0
+  const int64_t a_valid = (int64_t)a_rows * pa - (int64_t)a_col0 * sizeof(T);
+  const int64_t b_valid = (int64_t)b_rows * pb - (int64_t)b_col0 * sizeof(T);
+  // a K-outer operand's resource for stage s: its BK k-rows, clipped to the
+  // valid bytes (rows past them read zero)
+  auto kouter_rsrc = [&](const T* X, int col0, uint32_t pitch, int64_t valid,
+                         int s) -> i32x4_t {
+    const int64_t stage = (int64_t)BK * pitch;
+    const int64_t off = (int64_t)s * stage;
+    int64_t rem = valid - off;
+    rem = rem < 0 ? 0 : (rem > stage ? stage : rem);
+    const uint64_t a = (uint64_t)(uintptr_t)(X + col0) + (uint64_t)off;
+    return i32x4_t{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), (int)(uint32_t)rem,
+                   0x00020000};
+  };
+  i32x4_t rsa = TA ? i32x4_t{0, 0, 0, 0} : tile_rsrc_dw<T>(A, lda, a_rows);
+  i32x4_t rsb = TB ? i32x4_t{0, 0, 0, 0} : tile_rsrc_dw<T>(B, ldb, b_rows);
+  uint32_t va = 0, vb = 0;
+  // stage s: lane offsets (K-contiguous, past K -> out of range) or the
+  // stage's resource (K-outer)
   auto stage_offsets = [&](int s) {
     const uint32_t ko = (uint32_t)s * (uint32_t)RB;
-    va = s < kl ? ra + ko : kOutOfRange;
-    vb = s < kl ? rb + ko : kOutOfRange;
+    if constexpr (TA) rsa = kouter_rsrc(A, a_col0, pa, a_valid, s);
+    else va = s < kl ? ra + ko : kOutOfRange;
+    if constexpr (TB) rsb = kouter_rsrc(B, b_col0, pb, b_valid, s);
+    else vb = s < kl ? rb + ko : kOutOfRange;
   };
   // copy c of a stage: A and B blocks alternate while both last, then the
   // rest of the larger operand
@@ -354,19 +458,31 @@ __device__ __forceinline__ void tile_mainloop_ring(
   auto copy_one = [&](int s, int c) {
     const bool is_a = c < 2 * MinAB ? (c & 1) == 0 : KA > KB;
     const int u = c < 2 * MinAB ? c >> 1 : MinAB + (c - 2 * MinAB);
-    const uint32_t boff =
-        (uint32_t)((s % NST) * P::kStageBytes + u * W * 1024);
-    const uint32_t rows = (uint32_t)(u * W * P::kBlockRows);
-    if (is_a)
-      copy16_to_lds(dsta + boff, va + rows * pa, rsa);
-    else
-      copy16_to_lds(dstb + boff, vb + rows * pb, rsb);
+    if (is_a) {
+      if constexpr (TA)
+        copy16_to_lds(dsta + (uint32_t)((s % NST) * P::kStageBytes +
+                                        u * W * 1024),
+                      ta_lane + (uint32_t)(u * W * P::KA::kRows) * pa, rsa);
+      else
+        copy16_to_lds(dsta + (uint32_t)((s % NST) * P::kStageBytes +
+                                        u * W * 1024),
+                      va + (uint32_t)(u * W * P::kBlockRows) * pa, rsa);
+    } else {
+      if constexpr (TB)
+        copy16_to_lds(dstb + (uint32_t)((s % NST) * P::kStageBytes +
+                                        u * W * 1024),
+                      tb_lane + (uint32_t)(u * W * P::KB::kRows) * pb, rsb);
+      else
+        copy16_to_lds(dstb + (uint32_t)((s % NST) * P::kStageBytes +
+                                        u * W * 1024),
+                      vb + (uint32_t)(u * W * P::kBlockRows) * pb, rsb);
+    }
   };
 
-  // fragment side: lane (p, h) reads row (base + MB*x + p) at chunk
-  // CPS*s + h. The wave's first rows are multiples of 32, so the row's bits
-  // 0..2 are p's and its bit 4 is p's (MB = 32) or x's bit 0 (MB = 16): the
-  // swizzle is swz(p), flipped for odd x when MB = 16 and RB = 128.
+  // fragment side, K-contiguous: lane (p, h) reads row (base + MB*x + p) at
+  // chunk CPS*s + h. The wave's first rows are multiples of 32, so the row's
+  // bits 0..2 are p's and its bit 4 is p's (MB = 32) or x's bit 0 (MB = 16):
+  // the swizzle is swz(p), flipped for odd x when MB = 16 and RB = 128.
   static_assert(L::kWaveRows % 32 == 0 && L::kWaveCols % 32 == 0,
                 "wave sub-tiles start at multiples of 32 rows");
   const int g = P::swz(p);
@@ -376,13 +492,72 @@ __device__ __forceinline__ void tile_mainloop_ring(
 #pragma unroll
   for (int st = 0; st < S; ++st) fo[st] = ((CPS * st + h) ^ g) << 4;
   auto xflip = [](int x) { return MB == 16 && RB == 128 ? (x & 1) << 4 : 0; };
+
+  // fragment side, K-outer bf16 (see the transposing read above): lane
+  // (a = lane % 4, j = lane / 4 % 4, group h) of read e of K-step st
+  // addresses k-row 32 st + 8h + 4e + j, entries 4a .. 4a + 3 of 16-entry
+  // block x of the wave's blocks, whose first is segment seg0 (a multiple of
+  // 4 for A, of 8 for B, so seg0 + x = seg0 ^ x). That k-row's XOR is
+  // f = j | (h & 1) << 2 for every st and e, so the byte offset is
+  // (base ^ (x << 5)) + 512 (32 st + 4e) with base = (8h + j) 512 + 8a +
+  // ((seg0 ^ f) << 5): bits 5..8 of base hold the segment, and the terms
+  // added after the XOR have none of those bits.
+  const int tj = (lane >> 2) & 3;
+  const int t_f = tj | ((h & 1) << 2);
+  const int t_lane = (8 * h + tj) * 512 + 8 * (lane & 3);
+  const int ta_base = TA ? t_lane + (((wm * L::kWaveRows / 16) ^ t_f) << 5) : 0;
+  const int tb_base = TB ? t_lane + (((wn * L::kWaveCols / 16) ^ t_f) << 5) : 0;
+  static_assert(!TA || (L::kWaveRows / 16) % 4 == 0 && R <= 4,
+                "A's wave blocks: seg0 a multiple of 4, at most 4 blocks");
+  static_assert(!TB || (L::kWaveCols / 16) % 8 == 0 && C <= 8,
+                "B's wave blocks: seg0 a multiple of 8, at most 8 blocks");
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+  // the two transposing reads of a fragment: k-rows 8h + j and 8h + 4 + j
+  // (2 KiB further on) from byte offset o
+  auto tr_pair = [&](int o) {
+    const s16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(lds_char_t*)(smem + o));
+    const s16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(lds_char_t*)(smem + o + 4 * 512));
+    const u32x2_t q0 = __builtin_bit_cast(u32x2_t, r0);
+    const u32x2_t q1 = __builtin_bit_cast(u32x2_t, r1);
+    return u32x4_t{q0[0], q0[1], q1[0], q1[1]};
+  };
+  // fp32 K-outer: lane (p, h) gathers k-rows 16 st + 4h + i (i < 4) of entry
+  // wbase + 16x + p, 1 KiB apart
+  auto f32_col = [&](int o) {
+    const float* q = reinterpret_cast<const float*>(smem + o);
+    return u32x4_t{__builtin_bit_cast(uint32_t, q[0]),
+                   __builtin_bit_cast(uint32_t, q[256]),
+                   __builtin_bit_cast(uint32_t, q[512]),
+                   __builtin_bit_cast(uint32_t, q[768])};
+  };
   auto frag_a = [&](int stage_off, int st, int x) {
-    return *reinterpret_cast<const u32x4_t*>(
-        smem + stage_off + fa + (fo[st] ^ xflip(x)) + x * MB * RB);
+    if constexpr (TA) {
+      if constexpr (sizeof(T) == 2)
+        return tr_pair((ta_base ^ (x << 5)) + stage_off + 32 * st * 512);
+      else
+        return f32_col(stage_off + (16 * st + 4 * h) * 1024 +
+                       (wm * L::kWaveRows + 16 * x + p) * 4);
+    } else {
+      return *reinterpret_cast<const u32x4_t*>(
+          smem + stage_off + fa + (fo[st] ^ xflip(x)) + x * MB * RB);
+    }
   };
   auto frag_b = [&](int stage_off, int st, int x) {
-    return *reinterpret_cast<const u32x4_t*>(
-        smem + stage_off + fb + (fo[st] ^ xflip(x)) + x * MB * RB);
+    if constexpr (TB) {
+      if constexpr (sizeof(T) == 2)
+        return tr_pair((tb_base ^ (x << 5)) + stage_off + P::kOperandBytesA +
+                       32 * st * 512);
+      else
+        return f32_col(stage_off + P::kOperandBytesA +
+                       (16 * st + 4 * h) * 1024 +
+                       (wn * L::kWaveCols + 16 * x + p) * 4);
+    } else {
+      return *reinterpret_cast<const u32x4_t*>(
+          smem + stage_off + fb + (fo[st] ^ xflip(x)) + x * MB * RB);
+    }
   };
   const T* tag = nullptr;
 
@@ -537,25 +712,26 @@ __device__ __forceinline__ void tile_mainloop_ring(
 // The two configurations: 256 x 256 tiles for the dW and dH products (whose
 // output dimensions are multiples of 256 in the usual shapes), 256 x 320 tiles
 // (vocabulary on the 320 side) for the forward and the logit recompute.
-using TileLayout = Layout<256, 256, VPCE_WAVES_M, 2, VPCE_MFMA_BLOCK,
-                          VPCE_PROD_RING_RB, VPCE_PROD_RING_NST>;
+// The products read K-outer operands, which take 16 x 16 blocks and a
+// two-stage ring of 128-byte K-slabs (the build options below apply to the
+// forward and the logit recompute only).
+using TileLayout = Layout<256, 256, VPCE_WAVES_M, 2, 16, 128, 2>;
 // 128 x 256 tiles (32 x 128 per wave) for products whose 256 x 256 grid would
 // leave compute units idle: twice the tiles, at 50% more copied bytes per
 // flop.
-using HalfTileLayout = Layout<128, 256, 4, 2, VPCE_MFMA_BLOCK,
-                              VPCE_PROD_RING_RB, VPCE_PROD_RING_NST>;
+using HalfTileLayout = Layout<128, 256, 4, 2, 16, 128, 2>;
 using WideLayout = Layout<256, VPCE_WIDE_COLS, 4, 2>;
-template <typename L>
-using RingOf = Ring<L::RB, L::NST, L::TM, L::TN, L::kWaves>;
+template <typename L, typename T = __bf16, bool TA = false, bool TB = false>
+using RingOf = Ring<L::RB, L::NST, L::TM, L::TN, L::kWaves, T, TA, TB>;
 
-// smem must hold RingOf<L>::kBytes.
-template <typename T, typename L>
+// smem must hold RingOf<L, T, TA, TB>::kBytes.
+template <typename T, typename L, bool TA = false, bool TB = false>
 __device__ __forceinline__ void tile_mainloop(
     typename L::Acc (&acc)[L::R][L::C], const T* __restrict__ A, int64_t lda,
     int a_rows, const T* __restrict__ B, int64_t ldb, int b_rows, int64_t K,
-    char* smem) {
-  tile_mainloop_ring<T, L, L::RB, L::NST>(
-      acc, A, lda, a_rows, B, ldb, b_rows, K, smem);
+    char* smem, int a_col0 = 0, int b_col0 = 0) {
+  tile_mainloop_ring<T, L, L::RB, L::NST, TA, TB>(
+      acc, A, lda, a_rows, B, ldb, b_rows, K, smem, a_col0, b_col0);
 }
 
 // Workgroup L is dispatched to XCD (L mod 8). Renumber so that the workgroups

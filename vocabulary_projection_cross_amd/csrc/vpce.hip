@@ -15,11 +15,11 @@
 // Backward: the shards are replayed in the same order, each in fixed-width
 // chunks of C columns. Per chunk: recompute the logit tile, form
 // G = dloss/n * (exp(z - lse) - onehot) in registers and store it (bf16 or
-// fp32) both token-major and vocabulary-major; then dW_chunk = G^T H and
-// dH += G W_chunk, both on the same MFMA tile engine. Transposed copies of H
-// (once) and of the W chunk (per chunk) make every contraction an NT product.
-// Device working set: partials R x S x N, the G chunk N x C twice, H^T and the
-// W^T chunk -- fixed by N, d, R, S and C, never by V.
+// fp32) token-major; then dW_chunk = G^T H and dH += G W_chunk, both on the
+// same MFMA tile engine, which reads G, H and the W chunk as they are stored
+// (the products take them as K-outer operands where their K runs down the
+// rows). Device working set: partials R x S x N and one G chunk N x C --
+// fixed by N, R, S and C, never by V.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,6 +43,21 @@ constexpr int kChunkStep = 256;
 constexpr int kMaxSplits = 16;
 constexpr int64_t kMaxTokens = 2000000;
 constexpr int64_t kMaxHidden = 1000000;  // 320 rows of d fp32 stay below 2^31 B
+// 32-bit buffer offsets (tile_core.hpp). K-contiguous operand tiles (rows of
+// H, W or G, at most 320 of them) have resources spanning under 2^31 bytes,
+// and the rejected offset kOutOfRange plus a block offset of up to
+// kMaxBlockOffsetRows rows stays below 2^32; their longest pitch is a row of
+// H or W (d elements) at fp32, G rows being at most kChunkCols elements.
+// K-outer operands (H, G and W read by the backward products) get one
+// resource per stage, spanning its BK k-rows: 32 fp32 or 64 bf16 rows of at
+// most d elements.
+static_assert(kMaxHidden * 4 * kMaxBlockOffsetRows + (int64_t)kOutOfRange <
+                  ((int64_t)1 << 32),
+              "out-of-range offsets stay rejected");
+static_assert(kMaxHidden * 4 * 320 < ((int64_t)1 << 31) &&
+                  (int64_t)kChunkCols * 4 * 256 < ((int64_t)1 << 31) &&
+                  kMaxHidden * 128 < ((int64_t)1 << 31),
+              "operand tile and stage resources span under 2^31 bytes");
 // Grouped raster (consecutive workgroups of an XCD share operand rows): how
 // many token / output-row tiles sweep the column tiles together. Measured on
 // the 1M-context slice: 2 suits the forward, 8 the dW product, 4 the dH
@@ -409,83 +424,14 @@ __global__ void scale_from_totals_kernel(const double* totals,
   }
 }
 
-// dst[c][r] = src[r][c] for r < rows, 0 for rows <= r < dst_cols; c < cols.
-// Element type U is the raw storage (uint16_t for bf16, uint32_t for fp32).
-template <typename U>
-__global__ __launch_bounds__(256) void transpose_kernel(
-    const U* __restrict__ src, int64_t ld_src, int64_t rows, int64_t cols,
-    U* __restrict__ dst, int64_t ld_dst, int64_t dst_cols) {
-  // row stride an odd number of 4-byte words (65 for fp32, 66 halves = 33
-  // words for bf16), so the 64 lanes reading down a column hit 64 banks
-  __shared__ U t[64][sizeof(U) == 2 ? 66 : 65];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t r = r0 + k, c = c0 + tx;
-    U v = 0;
-    if (r < rows && c < cols) v = src[r * ld_src + c];
-    t[k][tx] = v;
-  }
-  __syncthreads();
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t c = c0 + k, r = r0 + tx;
-    if (c < cols && r < dst_cols) dst[c * ld_dst + r] = t[tx][k];
-  }
-}
-
-// The same for 16-bit elements with 16-byte accesses: a 64 x 64 tile is read
-// as 8-element row pieces (cols a multiple of 8, rows of src 16-byte
-// aligned), and each thread gathers 8 elements down a column of the tile
-// into one 16-byte store (dst_cols and ld_dst multiples of 64, dst 16-byte
-// aligned). Tile rows are padded to 68 elements (8-byte aligned).
-__global__ __launch_bounds__(256) void transpose16_kernel(
-    const uint16_t* __restrict__ src, int64_t ld_src, int64_t rows,
-    int64_t cols, uint16_t* __restrict__ dst, int64_t ld_dst,
-    int64_t dst_cols) {
-  constexpr int kPitch = 68;
-  __shared__ __attribute__((aligned(16))) uint16_t t[64 * kPitch];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  const int piece = tid & 7;  // 8-element piece of a row
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int row = (tid >> 3) + 32 * pass;
-    const int64_t r = r0 + row, c = c0 + piece * 8;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (r < rows && c < cols)
-      v = *reinterpret_cast<const u32x4_t*>(src + r * ld_src + c);
-    u32x2_t* q = reinterpret_cast<u32x2_t*>(t + row * kPitch + piece * 8);
-    q[0] = u32x2_t{v[0], v[1]};
-    q[1] = u32x2_t{v[2], v[3]};
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int col = (tid >> 3) + 32 * pass;  // row of dst
-    const int64_t c = c0 + col, r = r0 + piece * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)t[(piece * 8 + 2 * e) * kPitch + col] |
-             ((uint32_t)t[(piece * 8 + 2 * e + 1) * kPitch + col] << 16);
-    if (c < cols && r < dst_cols)
-      *reinterpret_cast<u32x4_t*>(dst + c * ld_dst + r) =
-          u32x4_t{w[0], w[1], w[2], w[3]};
-  }
-}
-
 // The bf16 G tile leaves through LDS one wave column (FL::kWaveCols chunk
-// columns, the waves with one wn) at a time. Transposed: each chunk column
-// holds 256 tokens, padded by 16 bytes so that the lanes writing 32 different
-// columns spread over the banks. Row-major: each token row holds the
-// FL::kWaveCols columns, padded the same way.
-constexpr int kGtColBytes = kTile * 2 + 16;
-constexpr int kGtLds = FL::kWaveCols * kGtColBytes;
+// columns, the waves with one wn) at a time: each token row holds the
+// FL::kWaveCols columns, padded by 16 bytes so that the lanes writing 32
+// different columns spread over the banks.
 constexpr int kGRowBytes = FL::kWaveCols * 2 + 16;
 constexpr int kGLds = kTile * kGRowBytes;
-constexpr int kRecLds = RingOf<FL>::kBytes > kGtLds
-                            ? (RingOf<FL>::kBytes > kGLds ? RingOf<FL>::kBytes : kGLds)
-                            : (kGtLds > kGLds ? kGtLds : kGLds);
+constexpr int kRecLds =
+    RingOf<FL>::kBytes > kGLds ? RingOf<FL>::kBytes : kGLds;
 static_assert(FL::kWaveCols % 8 == 0, "16-byte row chunks");
 
 struct GParams {
@@ -494,12 +440,11 @@ struct GParams {
   const int64_t* labels;
   const float* lse;
   const float* scale;
-  int64_t N, N_pad, d, V, ignore_index;
+  int64_t N, d, V, ignore_index;
   int64_t cv0;           // global vocabulary index of chunk column 0
   int64_t C_eff, C_pad;  // valid / padded chunk width
   int T, CT;             // token tiles, chunk column tiles
-  void* G;               // [N][C_pad]
-  void* GT;              // [C_pad][N_pad]
+  void* G;               // [N][C_pad], token-major
 };
 
 // two floats as bf16 (round to nearest even), lo in the low half
@@ -509,10 +454,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store4(float* p, float a, float b, float c,
-                                       float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-}
 
 template <typename T>
 __global__ __launch_bounds__(FL::kThreads) __attribute__((amdgpu_waves_per_eu(kFwdWaves, kFwdWaves)))
@@ -544,7 +485,6 @@ void recompute_g_kernel(GParams a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / FL::WN, wn = wave % FL::WN;
   T* G = reinterpret_cast<T*>(a.G);
-  T* GT = reinterpret_cast<T*>(a.GT);
   // G packed to bf16 pairs (rows 2k, 2k + 1 of row group rq of accumulator
   // (i, jj) in gpk[i][jj][2rq + k]), or stored at once (fp32). Chunk columns
   // of this lane: ccol[jj] = c0 + wn * kWaveCols + col(jj) (< 2^31).
@@ -589,53 +529,19 @@ void recompute_g_kernel(GParams a) {
           // opaque from here on: the compiler would otherwise keep every
           // unpacked bf16 value alive for the row-major stores and spill
           asm volatile("" : "+v"(gpk[i][jj][2 * rq]), "+v"(gpk[i][jj][2 * rq + 1]));
-        } else {
-          const int64_t tokb = tok0 + rowb;
-          if (c < a.C_pad && tokb < a.N_pad)
-            store4(GT + (int64_t)c * a.N_pad + tokb, gv[0], gv[1], gv[2], gv[3]);
         }
       }
     }
   }
   if constexpr (sizeof(T) == 2) {
-    // The barriers order the LDS staging only; the G and G^T stores stay in
-    // flight across them and past the end of the workgroup.
-    constexpr int kColChunks = kTile * 2 / 16;          // 16-byte chunks per G^T row
+    // The barriers order the LDS staging only; the G stores stay in flight
+    // across them and past the end of the workgroup.
     constexpr int kRowChunks = FL::kWaveCols * 2 / 16;  // per G row (one pass)
 #pragma unroll 1
     for (int pass = 0; pass < FL::WN; ++pass) {
       const int64_t cp0 = c0 + pass * FL::kWaveCols;  // first column of the pass
-      // G^T rows: the waves of this column write their columns transposed
-      // (4 tokens per 8-byte store), then every lane stores 16-byte chunks of
-      // the 256-token rows, coalesced.
-      if (wn == pass) {
-#pragma unroll
-        for (int jj = 0; jj < FL::C; ++jj) {
-          const int cl = FL::col(jj, lane);
-#pragma unroll
-          for (int i = 0; i < FL::R; ++i)
-#pragma unroll
-            for (int rq = 0; rq < FL::kRowGroups; ++rq) {
-              const int rowb = wm * FL::kWaveRows + FL::row_base(i, rq, lane);
-              *reinterpret_cast<u32x2_t*>(smem + cl * kGtColBytes + rowb * 2) =
-                  u32x2_t{gpk[i][jj][2 * rq], gpk[i][jj][2 * rq + 1]};
-            }
-        }
-      }
-      lds_barrier();
-#pragma unroll 4
-      for (int id = tid; id < FL::kWaveCols * kColChunks; id += FL::kThreads) {
-        const int cl = id / kColChunks, u = id % kColChunks;
-        const int64_t c = cp0 + cl;
-        const int64_t tokb = tok0 + 8 * u;
-        if (c < a.C_pad && tokb < a.N_pad) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
-              smem + cl * kGtColBytes + u * 16);
-          *reinterpret_cast<u32x4_t*>(GT + c * a.N_pad + tokb) = v;
-        }
-      }
-      lds_barrier();
-      // G rows: the same columns row-major, then 16-byte chunks per lane.
+      // G rows: the waves of this column write their columns row-major, then
+      // every lane stores 16-byte chunks of the rows, coalesced.
       if (wn == pass) {
 #pragma unroll
         for (int jj = 0; jj < FL::C; ++jj) {
@@ -680,6 +586,9 @@ struct ProdStage {
 };
 
 // out[M x Nc] (row stride ldo) = A . B^T over K, stored or accumulated (fp32).
+// A K-contiguous operand is [M x K] (or [Nc x K]) with row pitch lda (ldb);
+// a K-outer one is [K x M] (or [K x Nc]): its row k holds the M (Nc) entries
+// at row pitch lda (ldb), and only its first a_krows (b_krows) rows are read.
 struct ProdParams {
   const void* A;
   int64_t lda;
@@ -693,24 +602,29 @@ struct ProdParams {
   int TM, TN;
   int accumulate;
   int group;  // grouped raster: output-row tiles per group
+  int a_krows, b_krows;  // valid k-rows of K-outer operands
 };
 
-template <typename T, typename PL>
+template <typename T, typename PL, bool TA, bool TB>
 __global__ __launch_bounds__(PL::kThreads) __attribute__((amdgpu_waves_per_eu(PL::kWaves / 4, PL::kWaves / 4)))
 void prod_kernel(ProdParams a) {
   constexpr int kProdBandRows = ProdStage<PL>::kBandRows;
   constexpr int kProdPitch = ProdStage<PL>::kPitch;
-  __shared__ __attribute__((aligned(16))) char smem[RingOf<PL>::kBytes];
+  __shared__ __attribute__((aligned(16))) char
+      smem[RingOf<PL, T, TA, TB>::kBytes];
   const int total = a.TM * a.TN;
   const int idx = xcd_remap(blockIdx.x, total);
   int tm, tn;
   grouped_tile(idx, a.TM, a.TN, a.group, tm, tn);
   const int64_t m0 = (int64_t)tm * PL::TM, n0 = (int64_t)tn * PL::TN;
   typename PL::Acc acc[PL::R][PL::C];
-  tile_mainloop<T, PL>(acc, reinterpret_cast<const T*>(a.A) + m0 * a.lda,
-                       a.lda, clamp_rows(a.M - m0, PL::TM),
-                       reinterpret_cast<const T*>(a.B) + n0 * a.ldb, a.ldb,
-                       clamp_rows(a.Nc - n0, PL::TN), a.K, smem);
+  const T* Ab = reinterpret_cast<const T*>(a.A);
+  const T* Bb = reinterpret_cast<const T*>(a.B);
+  tile_mainloop<T, PL, TA, TB>(
+      acc, TA ? Ab : Ab + m0 * a.lda, a.lda,
+      TA ? a.a_krows : clamp_rows(a.M - m0, PL::TM), TB ? Bb : Bb + n0 * a.ldb,
+      a.ldb, TB ? a.b_krows : clamp_rows(a.Nc - n0, PL::TN), a.K, smem,
+      (int)m0, (int)n0);
   // The tile leaves through LDS one band of 64 rows (one row of waves) at a
   // time: those waves write their accumulators into the band, then every
   // thread moves 16-byte pieces of whole rows (1 KiB per wave instruction),
@@ -786,11 +700,11 @@ struct Plan {
   int64_t N, d, V;
   int R, dt, esz;
   int T, S, nb;
-  int64_t N_pad, C;
+  int64_t C;
   // forward layout
   size_t o_pm, o_ps, o_tgt, o_bsum, o_bcnt, fwd_bytes;
   // backward layout
-  size_t o_scale, o_HT, o_G, o_GT, o_WT, bwd_bytes;
+  size_t o_scale, o_G, bwd_bytes;
   size_t bytes;
 };
 
@@ -807,8 +721,7 @@ int splits_for(int64_t T, int R) {
 int32_t check_shape(int64_t N, int64_t d, int64_t V, int32_t R, int32_t dt) {
   if (dt != VPCE_BF16 && dt != VPCE_F32) return VPCE_ERR_UNSUPPORTED;
   if (N < 0 || d < 1 || V < 1 || R < 1 || (int64_t)R > V) return VPCE_ERR_SHAPE;
-  // 32-bit buffer offsets: 256 rows of any operand (H^T rows are N long)
-  // stay below 2^31 bytes
+  // 32-bit buffer offsets stay in range (see the static checks above)
   if (V >= ((int64_t)1 << 31) || N > kMaxTokens || d > kMaxHidden)
     return VPCE_ERR_SHAPE;
   if (d % (dt == VPCE_BF16 ? 8 : 4) != 0) return VPCE_ERR_SHAPE;
@@ -826,7 +739,6 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int R, int dt,
   p.T = (int)((N + kTile - 1) / kTile);
   p.S = splits_for(p.T > 0 ? p.T : 1, R);
   p.nb = (int)((N + 255) / 256);
-  p.N_pad = (N + 63) / 64 * 64;
   p.C = C;
   size_t o = 0;
   const size_t part = (size_t)R * p.S * (size_t)N * 4;
@@ -838,10 +750,7 @@ Plan make_plan(int64_t N, int64_t d, int64_t V, int R, int dt,
   p.fwd_bytes = o;
   o = 0;
   p.o_scale = o; o = up(o + 16);
-  p.o_HT = o; o = up(o + (size_t)d * p.N_pad * p.esz);
   p.o_G = o; o = up(o + (size_t)N * p.C * p.esz);
-  p.o_GT = o; o = up(o + (size_t)p.C * p.N_pad * p.esz);
-  p.o_WT = o; o = up(o + (size_t)d * p.C * p.esz);
   p.bwd_bytes = o;
   p.bytes = p.fwd_bytes > p.bwd_bytes ? p.fwd_bytes : p.bwd_bytes;
   return p;
@@ -881,31 +790,66 @@ inline bool aligned(const void* p, size_t a) {
     if (hipGetLastError() != hipSuccess) return VPCE_ERR_HIP; \
   } while (0)
 
+// Optional timing of the launches of one call (the *_traced entry points):
+// event pair i brackets the i-th kernel launch on the call's stream, and
+// kinds[i] says which kernel it was. Launches past `cap` are counted only.
+struct Trace {
+  const hipEvent_t* ev;  // 2 * cap events
+  int32_t* kinds;        // cap entries
+  int cap;
+  int n;
+};
+
+inline int32_t trace_begin(Trace* t, hipStream_t st) {
+  if (t && t->n < t->cap && hipEventRecord(t->ev[2 * t->n], st) != hipSuccess)
+    return VPCE_ERR_HIP;
+  return VPCE_OK;
+}
+
+inline int32_t trace_end(Trace* t, int32_t kind, hipStream_t st) {
+  if (!t) return VPCE_OK;
+  if (t->n < t->cap) {
+    if (hipEventRecord(t->ev[2 * t->n + 1], st) != hipSuccess)
+      return VPCE_ERR_HIP;
+    t->kinds[t->n] = kind;
+  }
+  ++t->n;
+  return VPCE_OK;
+}
+
+// Launch a kernel, check the launch, and bracket it for the trace (if any).
+#define VPCE_LAUNCH(KIND, KERNEL, GRID, BLOCK, ...)                       \
+  do {                                                                   \
+    if (trace_begin(tr, st) != VPCE_OK) return VPCE_ERR_HIP;             \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, st, __VA_ARGS__);         \
+    if (hipGetLastError() != hipSuccess) return VPCE_ERR_HIP;            \
+    if (trace_end(tr, KIND, st) != VPCE_OK) return VPCE_ERR_HIP;         \
+  } while (0)
+
 template <typename T>
 int32_t run_forward(const Plan& p, const void* H, const void* W,
                     const int64_t* labels, int64_t ignore_index, float* loss,
-                    float* lse, char* ws, hipStream_t st) {
+                    float* lse, char* ws, hipStream_t st,
+                    Trace* tr = nullptr) {
   float* pm = reinterpret_cast<float*>(ws + p.o_pm);
   float* ps = reinterpret_cast<float*>(ws + p.o_ps);
   float* tgt = reinterpret_cast<float*>(ws + p.o_tgt);
   double* bsum = reinterpret_cast<double*>(ws + p.o_bsum);
   int* bcnt = reinterpret_cast<int*>(ws + p.o_bcnt);
   if (p.N > 0) {
-    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0, st,
-                       tgt, p.N, NAN);
-    VPCE_LAUNCH_CHECK();
+    VPCE_LAUNCH(VPCE_KERNEL_OTHER, fill_kernel,
+                dim3((unsigned)((p.N + 255) / 256)), dim3(256), tgt, p.N, NAN);
     FwdParams fp{H, W, labels, p.N, p.d, p.V, ignore_index, p.R, p.S, p.T,
                  pm, ps, tgt, 0, p.V};
     const unsigned grid = (unsigned)((int64_t)p.T * p.R * p.S);
-    hipLaunchKernelGGL(fwd_lse_kernel<T>, dim3(grid), dim3(FL::kThreads), 0, st, fp);
-    VPCE_LAUNCH_CHECK();
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)p.nb), dim3(256), 0, st, pm, ps,
-                       tgt, labels, p.N, p.R * p.S, ignore_index, lse, bsum, bcnt);
-    VPCE_LAUNCH_CHECK();
+    VPCE_LAUNCH(VPCE_KERNEL_FORWARD_TILE, fwd_lse_kernel<T>, dim3(grid),
+                dim3(FL::kThreads), fp);
+    VPCE_LAUNCH(VPCE_KERNEL_MERGE, merge_kernel, dim3((unsigned)p.nb),
+                dim3(256), pm, ps, tgt, labels, p.N, p.R * p.S, ignore_index,
+                lse, bsum, bcnt);
   }
-  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, bsum, bcnt, p.nb,
-                     loss, static_cast<double*>(nullptr));
-  VPCE_LAUNCH_CHECK();
+  VPCE_LAUNCH(VPCE_KERNEL_OTHER, loss_kernel, dim3(1), dim3(256), bsum, bcnt,
+              p.nb, loss, static_cast<double*>(nullptr));
   return VPCE_OK;
 }
 
@@ -920,58 +864,40 @@ int device_cus() {
 }
 
 // out (+)= A . B^T over pp.M output rows and pp.TN column tiles of 256: on
-// 256 x 256 tiles, or on 128 x 256 tiles where the former would give fewer
-// tiles than the device has compute units. Sets pp.TM.
-template <typename T>
-int32_t launch_prod(ProdParams pp, int cus, hipStream_t st) {
+// 256 x 256 tiles, or, when A is K-contiguous, on 128 x 256 tiles where the
+// former would give fewer tiles than the device has compute units. Sets pp.TM.
+template <typename T, bool TA, bool TB>
+int32_t launch_prod(ProdParams pp, int cus, int32_t kind, hipStream_t st,
+                    Trace* tr) {
   const int64_t tiles = (pp.M + TL::TM - 1) / TL::TM * pp.TN;
-  if (cus > 0 && tiles < cus) {
+  if (!TA && cus > 0 && tiles < cus) {
     pp.TM = (int)((pp.M + HL::TM - 1) / HL::TM);
-    hipLaunchKernelGGL((prod_kernel<T, HL>), dim3((unsigned)(pp.TM * pp.TN)),
-                       dim3(HL::kThreads), 0, st, pp);
+    VPCE_LAUNCH(kind, (prod_kernel<T, HL, false, TB>),
+                dim3((unsigned)(pp.TM * pp.TN)), dim3(HL::kThreads), pp);
   } else {
     pp.TM = (int)((pp.M + TL::TM - 1) / TL::TM);
-    hipLaunchKernelGGL((prod_kernel<T, TL>), dim3((unsigned)(pp.TM * pp.TN)),
-                       dim3(TL::kThreads), 0, st, pp);
-  }
-  VPCE_LAUNCH_CHECK();
-  return VPCE_OK;
-}
-
-// H^T [d][N_pad] into the workspace, zero in the padding columns.
-template <typename U>
-int32_t transpose_h(const Plan& p, const void* H, char* ws, hipStream_t st) {
-  if (p.N_pad > 0) {
-    dim3 g((unsigned)((p.N_pad + 63) / 64), (unsigned)((p.d + 63) / 64));
-    if constexpr (sizeof(U) == 2)
-      hipLaunchKernelGGL(transpose16_kernel, g, dim3(256), 0, st,
-                         reinterpret_cast<const U*>(H), p.d, p.N, p.d,
-                         reinterpret_cast<U*>(ws + p.o_HT), p.N_pad, p.N_pad);
-    else
-      hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st,
-                         reinterpret_cast<const U*>(H), p.d, p.N, p.d,
-                         reinterpret_cast<U*>(ws + p.o_HT), p.N_pad, p.N_pad);
-    VPCE_LAUNCH_CHECK();
+    VPCE_LAUNCH(kind, (prod_kernel<T, TL, TA, TB>),
+                dim3((unsigned)(pp.TM * pp.TN)), dim3(TL::kThreads), pp);
   }
   return VPCE_OK;
 }
 
 // Backward over the vocabulary entries [v_first, v_first + v_count), whose
 // rows of W start at Wspan and whose rows of dW start at dWspan, in chunks of
-// p.C columns: recompute G for the chunk, dW rows = G^T H, dH += G W_chunk.
-// The first chunk overwrites dH unless dH_acc; dW rows are overwritten unless
-// dW_acc. H^T must already be in the workspace and *scale on the device.
-template <typename T, typename U>
+// p.C columns: recompute G for the chunk (token-major, [N x C_pad]), then
+// dW rows = G^T H and dH += G W_chunk. G, H and W are all read as they are
+// stored: the dW product takes G and H as K-outer operands (K = tokens), the
+// dH product G as a K-contiguous one and the W chunk as a K-outer one
+// (K = vocabulary entries). The first chunk overwrites dH unless dH_acc; dW
+// rows are overwritten unless dW_acc. *scale must be on the device.
+template <typename T>
 int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
                       int64_t v_first, int64_t v_count, int64_t V_lab,
                       const int64_t* labels, const float* lse,
                       const float* scale, int64_t ignore_index, float* dH,
                       bool dH_acc, float* dWspan, bool dW_acc, char* ws,
-                      hipStream_t st) {
-  void* HT = ws + p.o_HT;
+                      hipStream_t st, Trace* tr) {
   void* G = ws + p.o_G;
-  void* GT = ws + p.o_GT;
-  void* WT = ws + p.o_WT;
   const int TD = (int)((p.d + kTile - 1) / kTile);
   bool acc_h = dH_acc;
   const int cus = device_cus();
@@ -979,38 +905,31 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
     const int64_t ceff = (v_count - c0) < p.C ? (v_count - c0) : p.C;
     const int64_t cpad = (ceff + 63) / 64 * 64;
     const int64_t cv0 = v_first + c0;
-    const U* Wc = reinterpret_cast<const U*>(Wspan) + c0 * p.d;
-    // W^T chunk [d][C_pad], zero in the padding columns
-    {
-      dim3 g((unsigned)((cpad + 63) / 64), (unsigned)((p.d + 63) / 64));
-      if constexpr (sizeof(U) == 2)
-        hipLaunchKernelGGL(transpose16_kernel, g, dim3(256), 0, st, Wc, p.d,
-                           ceff, p.d, reinterpret_cast<U*>(WT), cpad, cpad);
-      else
-        hipLaunchKernelGGL(transpose_kernel<U>, g, dim3(256), 0, st, Wc, p.d,
-                           ceff, p.d, reinterpret_cast<U*>(WT), cpad, cpad);
-      VPCE_LAUNCH_CHECK();
-    }
+    const T* Wc = reinterpret_cast<const T*>(Wspan) + c0 * p.d;
     const int CT = (int)((cpad + FL::TN - 1) / FL::TN);
     if (p.N > 0) {
-      GParams gp{H, Wc, labels, lse, scale, p.N, p.N_pad, p.d, V_lab,
-                 ignore_index, cv0, ceff, cpad, p.T, CT, G, GT};
-      hipLaunchKernelGGL(recompute_g_kernel<T>, dim3((unsigned)(p.T * CT)),
-                         dim3(FL::kThreads), 0, st, gp);
-      VPCE_LAUNCH_CHECK();
+      GParams gp{H, Wc, labels, lse, scale, p.N, p.d, V_lab,
+                 ignore_index, cv0, ceff, cpad, p.T, CT, G};
+      VPCE_LAUNCH(VPCE_KERNEL_RECOMPUTE, recompute_g_kernel<T>,
+                  dim3((unsigned)(p.T * CT)), dim3(FL::kThreads), gp);
     }
-    // dW rows of the chunk = G^T H : A = G^T [C_pad x N_pad], B = H^T
+    // dW rows of the chunk = G^T H: A = G (K-outer: row k = token, C_pad
+    // entries), B = H (K-outer: row k = token, d entries), K = N
     {
-      ProdParams pp{GT, p.N_pad, ceff, HT, p.N_pad, p.d, p.N_pad,
-                    dWspan + c0 * p.d, p.d, 0, TD, dW_acc ? 1 : 0, kGroupDW};
-      const int32_t rc = launch_prod<T>(pp, cus, st);
+      ProdParams pp{G, cpad, ceff, H, p.d, p.d, p.N,
+                    dWspan + c0 * p.d, p.d, 0, TD, dW_acc ? 1 : 0, kGroupDW,
+                    (int)p.N, (int)p.N};
+      const int32_t rc =
+          launch_prod<T, true, true>(pp, cus, VPCE_KERNEL_PRODUCT_DW, st, tr);
       if (rc != VPCE_OK) return rc;
     }
-    // dH (+)= G W_chunk : A = G [N x C_pad], B = W^T chunk [d x C_pad]
+    // dH (+)= G W_chunk: A = G [N x C_pad] (K-contiguous), B = W chunk
+    // (K-outer: row k = vocabulary entry, d entries; rows past ceff read 0)
     if (p.N > 0) {
-      ProdParams pp{G, cpad, p.N, WT, cpad, p.d, cpad, dH, p.d, 0, TD,
-                    acc_h ? 1 : 0, kGroupDH};
-      const int32_t rc = launch_prod<T>(pp, cus, st);
+      ProdParams pp{G, cpad, p.N, Wc, p.d, p.d, cpad, dH, p.d, 0, TD,
+                    acc_h ? 1 : 0, kGroupDH, 0, (int)ceff};
+      const int32_t rc =
+          launch_prod<T, false, true>(pp, cus, VPCE_KERNEL_PRODUCT_DH, st, tr);
       if (rc != VPCE_OK) return rc;
     }
     acc_h = true;
@@ -1018,23 +937,21 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
   return VPCE_OK;
 }
 
-template <typename T, typename U>
+template <typename T>
 int32_t run_backward(const Plan& p, const void* H, const void* W,
                      const int64_t* labels, const float* lse,
                      const float* dloss, int64_t ignore_index, float* dH,
-                     float* dW, char* ws, hipStream_t st) {
+                     float* dW, char* ws, hipStream_t st,
+                     Trace* tr = nullptr) {
   float* scale = reinterpret_cast<float*>(ws + p.o_scale);
-  hipLaunchKernelGGL(scale_kernel, dim3(1), dim3(1024), 0, st, labels, p.N,
-                     ignore_index, dloss, scale);
-  VPCE_LAUNCH_CHECK();
-  int32_t rc = transpose_h<U>(p, H, ws, st);
-  if (rc != VPCE_OK) return rc;
+  VPCE_LAUNCH(VPCE_KERNEL_OTHER, scale_kernel, dim3(1), dim3(1024), labels,
+              p.N, ignore_index, dloss, scale);
   const Shards sh{p.V, p.R};
   for (int r = 0; r < p.R; ++r) {
     const int64_t v0 = sh.begin(r), vw = sh.width(r);
-    rc = backward_span<T, U>(p, H, reinterpret_cast<const U*>(W) + v0 * p.d,
-                             v0, vw, p.V, labels, lse, scale, ignore_index,
-                             dH, r > 0, dW + v0 * p.d, false, ws, st);
+    const int32_t rc = backward_span<T>(
+        p, H, reinterpret_cast<const T*>(W) + v0 * p.d, v0, vw, p.V, labels,
+        lse, scale, ignore_index, dH, r > 0, dW + v0 * p.d, false, ws, st, tr);
     if (rc != VPCE_OK) return rc;
   }
   return VPCE_OK;
@@ -1096,11 +1013,12 @@ int32_t vpce_plan(int64_t N, int64_t d, int64_t V, int32_t R, int32_t dtype,
   return VPCE_OK;
 }
 
-int32_t vpce_forward(const void* H, const void* W, const int64_t* labels,
-                     int64_t N, int64_t d, int64_t V, int32_t R,
-                     int64_t ignore_index, int32_t dtype, float* loss,
-                     float* lse, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+namespace {
+int32_t forward_entry(const void* H, const void* W, const int64_t* labels,
+                      int64_t N, int64_t d, int64_t V, int32_t R,
+                      int64_t ignore_index, int32_t dtype, float* loss,
+                      float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream, Trace* tr) {
   const int32_t s = check_shape(N, d, V, R, dtype);
   if (s != VPCE_OK) return s;
   if (!W || !loss || !workspace) return VPCE_ERR_NULL;
@@ -1113,15 +1031,15 @@ int32_t vpce_forward(const void* H, const void* W, const int64_t* labels,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == VPCE_BF16)
-    return run_forward<__bf16>(p, H, W, labels, ignore_index, loss, lse, ws, st);
-  return run_forward<float>(p, H, W, labels, ignore_index, loss, lse, ws, st);
+    return run_forward<__bf16>(p, H, W, labels, ignore_index, loss, lse, ws, st, tr);
+  return run_forward<float>(p, H, W, labels, ignore_index, loss, lse, ws, st, tr);
 }
 
-int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
-                      const float* lse, const float* dloss, int64_t N,
-                      int64_t d, int64_t V, int32_t R, int64_t ignore_index,
-                      int32_t dtype, float* dH, float* dW, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+int32_t backward_entry(const void* H, const void* W, const int64_t* labels,
+                       const float* lse, const float* dloss, int64_t N,
+                       int64_t d, int64_t V, int32_t R, int64_t ignore_index,
+                       int32_t dtype, float* dH, float* dW, void* workspace,
+                       size_t workspace_bytes, void* stream, Trace* tr) {
   const int32_t s = check_shape(N, d, V, R, dtype);
   if (s != VPCE_OK) return s;
   if (!W || !dW || !workspace) return VPCE_ERR_NULL;
@@ -1136,10 +1054,82 @@ int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == VPCE_BF16)
-    return run_backward<__bf16, uint16_t>(p, H, W, labels, lse, dloss,
-                                          ignore_index, dH, dW, ws, st);
-  return run_backward<float, uint32_t>(p, H, W, labels, lse, dloss,
-                                       ignore_index, dH, dW, ws, st);
+    return run_backward<__bf16>(p, H, W, labels, lse, dloss, ignore_index, dH,
+                                dW, ws, st, tr);
+  return run_backward<float>(p, H, W, labels, lse, dloss, ignore_index, dH,
+                             dW, ws, st, tr);
+}
+
+// Validates the trace arguments of the *_traced calls and sets up *t.
+int32_t make_trace(void* const* events, int32_t max_launches, int32_t* kinds,
+                   int32_t* n_launches, Trace* t) {
+  if (max_launches < 0) return VPCE_ERR_SHAPE;
+  if (!n_launches || (max_launches > 0 && (!events || !kinds)))
+    return VPCE_ERR_NULL;
+  for (int32_t i = 0; i < 2 * max_launches; ++i)
+    if (!events[i]) return VPCE_ERR_NULL;
+  t->ev = reinterpret_cast<const hipEvent_t*>(events);
+  t->kinds = kinds;
+  t->cap = max_launches;
+  t->n = 0;
+  return VPCE_OK;
+}
+}  // namespace
+
+int32_t vpce_forward(const void* H, const void* W, const int64_t* labels,
+                     int64_t N, int64_t d, int64_t V, int32_t R,
+                     int64_t ignore_index, int32_t dtype, float* loss,
+                     float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return forward_entry(H, W, labels, N, d, V, R, ignore_index, dtype, loss,
+                       lse, workspace, workspace_bytes, stream, nullptr);
+}
+
+int32_t vpce_forward_traced(const void* H, const void* W,
+                            const int64_t* labels, int64_t N, int64_t d,
+                            int64_t V, int32_t R, int64_t ignore_index,
+                            int32_t dtype, float* loss, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* events,
+                            int32_t max_launches, int32_t* kinds,
+                            int32_t* n_launches) {
+  Trace t;
+  const int32_t s = make_trace(events, max_launches, kinds, n_launches, &t);
+  if (s != VPCE_OK) return s;
+  const int32_t rc = forward_entry(H, W, labels, N, d, V, R, ignore_index,
+                                   dtype, loss, lse, workspace,
+                                   workspace_bytes, stream, &t);
+  *n_launches = t.n;
+  return rc;
+}
+
+int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
+                      const float* lse, const float* dloss, int64_t N,
+                      int64_t d, int64_t V, int32_t R, int64_t ignore_index,
+                      int32_t dtype, float* dH, float* dW, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return backward_entry(H, W, labels, lse, dloss, N, d, V, R, ignore_index,
+                        dtype, dH, dW, workspace, workspace_bytes, stream,
+                        nullptr);
+}
+
+int32_t vpce_backward_traced(const void* H, const void* W,
+                             const int64_t* labels, const float* lse,
+                             const float* dloss, int64_t N, int64_t d,
+                             int64_t V, int32_t R, int64_t ignore_index,
+                             int32_t dtype, float* dH, float* dW,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream, void* const* events,
+                             int32_t max_launches, int32_t* kinds,
+                             int32_t* n_launches) {
+  Trace t;
+  const int32_t s = make_trace(events, max_launches, kinds, n_launches, &t);
+  if (s != VPCE_OK) return s;
+  const int32_t rc = backward_entry(H, W, labels, lse, dloss, N, d, V, R,
+                                    ignore_index, dtype, dH, dW, workspace,
+                                    workspace_bytes, stream, &t);
+  *n_launches = t.n;
+  return rc;
 }
 
 int32_t vpce_state_init(float* state, int64_t N, void* stream) {
@@ -1245,19 +1235,13 @@ int32_t vpce_shard_backward(const void* H, const void* W_shard,
   hipLaunchKernelGGL(scale_from_totals_kernel, dim3(1), dim3(64), 0, st,
                      totals, dloss, scale);
   VPCE_LAUNCH_CHECK();
-  int32_t rc;
-  if (dtype == VPCE_BF16) {
-    rc = transpose_h<uint16_t>(p, H, ws, st);
-    if (rc != VPCE_OK) return rc;
-    return backward_span<__bf16, uint16_t>(p, H, W_shard, v_begin, v_count, V,
-                                           labels, lse, scale, ignore_index,
-                                           dH, true, dW_shard, true, ws, st);
-  }
-  rc = transpose_h<uint32_t>(p, H, ws, st);
-  if (rc != VPCE_OK) return rc;
-  return backward_span<float, uint32_t>(p, H, W_shard, v_begin, v_count, V,
-                                        labels, lse, scale, ignore_index, dH,
-                                        true, dW_shard, true, ws, st);
+  if (dtype == VPCE_BF16)
+    return backward_span<__bf16>(p, H, W_shard, v_begin, v_count, V, labels,
+                                 lse, scale, ignore_index, dH, true, dW_shard,
+                                 true, ws, st, nullptr);
+  return backward_span<float>(p, H, W_shard, v_begin, v_count, V, labels, lse,
+                              scale, ignore_index, dH, true, dW_shard, true,
+                              ws, st, nullptr);
 }
 
 int32_t vpce_ring_mode(int64_t N, int64_t d, int64_t V, int32_t R,
