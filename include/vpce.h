@@ -31,8 +31,10 @@
  *    all work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *    Argument errors are detected on the host and returned BEFORE anything is
  *    enqueued. A failed kernel launch returns VPCE_ERR_HIP.
- *  - Functions are reentrant; the library keeps no state between calls.
- *    Concurrent calls must use distinct workspaces.
+ *  - Functions are reentrant; the library keeps no state between calls
+ *    (except the device address of the static scratch of
+ *    vpce_forward_noalloc, see there). Concurrent calls must use distinct
+ *    workspaces.
  *  - Requirements: 0 <= N <= 2000000, 1 <= d <= 1000000, V >= 1,
  *    1 <= R <= V, V < 2^31, d a multiple of 8 (VPCE_BF16) or 4 (VPCE_F32),
  *    H, W, dH and dW 16-byte aligned (a shard's rows of W or dW then are
@@ -64,7 +66,11 @@ typedef enum {
   VPCE_ERR_WORKSPACE = 5,   /* workspace too small for the call (see the
                                workspace notes of each call), or a budget
                                that cannot hold the operation */
-  VPCE_ERR_HIP = 6          /* a kernel launch failed */
+  VPCE_ERR_HIP = 6,         /* a kernel launch failed (or, for
+                               vpce_forward_noalloc, the device address of its
+                               scratch could not be obtained) */
+  VPCE_ERR_SCRATCH = 7      /* vpce_forward_noalloc: the shape needs more
+                               than VPCE_NOALLOC_SCRATCH_BYTES */
 } vpce_status_t;
 
 /*
@@ -136,6 +142,45 @@ int32_t vpce_forward(const void* H, const void* W, const int64_t* labels,
                      int64_t ignore_index, int32_t dtype, float* loss,
                      float* lse, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * ---- Allocation-free forward ----------------------------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. The same
+ * computation and kernels as vpce_forward (bitwise the same loss and lse),
+ * with the forward's scratch (per-token partial states of every shard and
+ * vocabulary split, target logits, per-block loss sums) taken from a static
+ * device array of VPCE_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on, from the first call on that GPU until the process ends. The
+ * call allocates and frees nothing (no hipMalloc, no hipFree); the caller
+ * still provides H, W, labels, loss and lse.
+ *
+ * Scratch needed: vpce_forward_noalloc_bytes(N, d, V, R, dtype), about
+ * (8 R S + 4) N bytes with S = max(1, ceil(512 / (ceil(N / 256) R))) vocabulary
+ * splits per shard (at most 16); larger shapes return VPCE_ERR_SCRATCH
+ * before anything is enqueued. Nothing in the scratch needs clearing between
+ * calls: every call writes all it reads.
+ *
+ * All calls on one GPU share that GPU's scratch: calls that may overlap in
+ * time on one GPU (different streams, or different host threads without
+ * ordering) race and give undefined results. Serialise them, e.g. on one
+ * stream. The first call on each GPU looks up the array's device address
+ * (hipGetSymbolAddress, with that GPU current) and keeps it; that lookup is
+ * the library's only state between calls.
+ */
+#define VPCE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int32_t vpce_forward_noalloc(const void* H, const void* W,
+                             const int64_t* labels, int64_t N, int64_t d,
+                             int64_t V, int32_t R, int64_t ignore_index,
+                             int32_t dtype, float* loss, float* lse,
+                             void* stream);
+
+/* Scratch bytes vpce_forward_noalloc needs for this shape (0 for arguments
+   vpce_forward would reject). Pure host function. */
+size_t vpce_forward_noalloc_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
+                                  int32_t dtype);
 
 /*
  * Backward (section 3.2: the same rounds replayed, each logit strip recomputed

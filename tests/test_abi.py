@@ -30,6 +30,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = header_functions()
     assert names == ["vpce_backward", "vpce_backward_traced", "vpce_forward",
+                     "vpce_forward_noalloc", "vpce_forward_noalloc_bytes",
                      "vpce_forward_traced", "vpce_plan",
                      "vpce_ring_mode", "vpce_shard_backward",
                      "vpce_shard_fold", "vpce_state_finish",

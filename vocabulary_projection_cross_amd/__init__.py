@@ -21,6 +21,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["forward", "backward", "workspace_bytes", "plan", "ring_mode",
+           "forward_noalloc", "forward_noalloc_bytes", "NOALLOC_SCRATCH_BYTES",
            "forward_traced", "backward_traced", "KERNEL_KINDS",
            "state_init", "shard_fold", "state_finish", "shard_backward",
            "VPCEError", "library_path", "IGNORE_INDEX", "VPCE_BF16",
@@ -67,6 +68,11 @@ def _load():
     lib.vpce_forward.restype = i32
     lib.vpce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i32,
                                  vp, vp, vp, sz, vp]
+    lib.vpce_forward_noalloc.restype = i32
+    lib.vpce_forward_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64,
+                                         i32, vp, vp, vp]
+    lib.vpce_forward_noalloc_bytes.restype = sz
+    lib.vpce_forward_noalloc_bytes.argtypes = [i64, i64, i64, i32, i32]
     for name, n_args in (("vpce_forward_traced", 14),
                          ("vpce_backward_traced", 16)):
         f = getattr(lib, name)
@@ -205,6 +211,39 @@ def forward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, R: int,
                               ctypes.c_void_p(stream))
     _check(st)
     return loss, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_noalloc(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+                    R: int, loss: torch.Tensor, lse: torch.Tensor,
+                    ignore_index: int = IGNORE_INDEX) -> None:
+    """vpce_forward_noalloc: the forward into the caller's loss [] and lse
+    [N] (fp32, on H's device), with the library's static device scratch in
+    place of a workspace; nothing is allocated, here or in the library.
+    Calls on one GPU that overlap in time race on that scratch."""
+    _validate(H, W, labels)
+    N, d = H.shape
+    for name, t, n in (("loss", loss, 1), ("lse", lse, N)):
+        if (t.device != H.device or t.dtype != torch.float32
+                or t.numel() != n or not t.is_contiguous()):
+            raise VPCEError(f"{name} must be a contiguous fp32 tensor of {n} "
+                            "elements on H's device")
+    with torch.cuda.device(H.device):
+        st = _load().vpce_forward_noalloc(
+            _ptr(H), _ptr(W), _ptr(labels), N, d, W.shape[0], R,
+            ignore_index, _dtype_code(H.dtype), _ptr(loss), _ptr(lse),
+            _stream(H))
+    _check(st)
+
+
+def forward_noalloc_bytes(N: int, d: int, V: int, R: int,
+                          dtype: torch.dtype = torch.bfloat16) -> int:
+    """Scratch bytes vpce_forward_noalloc needs (at most
+    NOALLOC_SCRATCH_BYTES is available); 0 for invalid arguments."""
+    return int(_load().vpce_forward_noalloc_bytes(N, d, V, R,
+                                                  _dtype_code(dtype)))
 
 
 def backward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,

@@ -24,10 +24,19 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tile_core.hpp"
 #include "vpce.h"
 
 using namespace vpce;
+
+// Device memory of vpce_forward_noalloc: its per-token partial states, target
+// logits and block sums live here instead of in a caller's workspace. Every
+// GPU the library runs on holds its own copy until the process ends. In host
+// code this name is only a stand-in for the symbol; the device address comes
+// from hipGetSymbolAddress (scratch_on_current_device).
+static __device__ __align__(256) char scratch[VPCE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -785,6 +794,28 @@ inline bool aligned(const void* p, size_t a) {
   return ((uintptr_t)p % a) == 0;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int32_t scratch_on_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return VPCE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess ||
+        ptr == nullptr)
+      return VPCE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = reinterpret_cast<char*>(g_scratch_ptr[dev]);
+  return VPCE_OK;
+}
+
 #define VPCE_LAUNCH_CHECK()                              \
   do {                                                   \
     if (hipGetLastError() != hipSuccess) return VPCE_ERR_HIP; \
@@ -1103,6 +1134,35 @@ int32_t vpce_forward_traced(const void* H, const void* W,
   return rc;
 }
 
+int32_t vpce_forward_noalloc(const void* H, const void* W,
+                             const int64_t* labels, int64_t N, int64_t d,
+                             int64_t V, int32_t R, int64_t ignore_index,
+                             int32_t dtype, float* loss, float* lse,
+                             void* stream) {
+  const int32_t s = check_shape(N, d, V, R, dtype);
+  if (s != VPCE_OK) return s;
+  if (!W || !loss) return VPCE_ERR_NULL;
+  if (N > 0 && (!H || !labels || !lse)) return VPCE_ERR_NULL;
+  if ((H && !aligned(H, 16)) || !aligned(W, 16) || (labels && !aligned(labels, 8)) ||
+      !aligned(loss, 4) || (lse && !aligned(lse, 4)))
+    return VPCE_ERR_ALIGN;
+  const Plan p = make_plan(N, d, V, R, dtype);
+  if (p.fwd_bytes > (size_t)VPCE_NOALLOC_SCRATCH_BYTES) return VPCE_ERR_SCRATCH;
+  char* ws = nullptr;
+  const int32_t rc = scratch_on_current_device(&ws);
+  if (rc != VPCE_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == VPCE_BF16)
+    return run_forward<__bf16>(p, H, W, labels, ignore_index, loss, lse, ws, st);
+  return run_forward<float>(p, H, W, labels, ignore_index, loss, lse, ws, st);
+}
+
+size_t vpce_forward_noalloc_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
+                                  int32_t dtype) {
+  if (check_shape(N, d, V, R, dtype) != VPCE_OK) return 0;
+  return make_plan(N, d, V, R, dtype).fwd_bytes;
+}
+
 int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
                       const float* lse, const float* dloss, int64_t N,
                       int64_t d, int64_t V, int32_t R, int64_t ignore_index,
@@ -1267,6 +1327,9 @@ const char* vpce_status_string(int32_t status) {
     case VPCE_ERR_ALIGN: return "misaligned pointer";
     case VPCE_ERR_WORKSPACE: return "workspace too small";
     case VPCE_ERR_HIP: return "HIP kernel launch failed";
+    case VPCE_ERR_SCRATCH:
+      return "shape needs more than the static scratch of the "
+             "allocation-free forward (VPCE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
