@@ -16,7 +16,9 @@ and the backward, which record a HIP event pair on the library's stream (the
 current torch stream, passed to the C ABI) around every kernel launch. The
 line's roofline block is for the kernel with the most GPU time per step: its
 algorithmic flops per launch (2*N*d*V for the forward tile kernel, 2*N*d*C
-for a backward chunk of C vocabulary columns) over its mean launch duration.
+for the logit recompute of a backward chunk of C vocabulary columns and
+4*N*d*C for the launch that forms both its products) over its mean launch
+duration.
 Every kernel kind's own figures are listed under roofline.kernels. HBM
 traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs
 of this same script, scaled by the counters' reading for plain device copies
@@ -73,10 +75,12 @@ def kernel_code_hash() -> str:
 
 KERNEL_NAMES = {"forward_tile": "fwd_lse_kernel",
                 "recompute": "recompute_g_kernel",
-                "product_dw": "prod_kernel (dW = G^T H)",
-                "product_dh": "prod_kernel (dH += G W)",
-                "transpose": "transpose16_kernel",
+                "products": "prod_pair_kernel (dW = G^T H and dH += G W)",
                 "merge": "merge_kernel", "other": "fill/loss/scale kernels"}
+# algorithmic flops of one launch per backward-chunk column: the recompute
+# forms one N x C logit chunk (2 N d C), the product launch both dW and dH of
+# the chunk (2 x 2 N d C)
+CHUNK_PRODUCTS = {"recompute": 1, "products": 2}
 
 
 def chunk_widths(w, C):
@@ -95,19 +99,21 @@ def kernel_table(w, kinds_f, fev, kinds_b, bev, C):
     """Per kernel kind: launches per step, mean duration per launch and per
     step (HIP events around each launch, averaged over the timed steps), and
     the algorithmic flops of its launches (2 N d V for the forward tile
-    kernel, 2 N d C per backward chunk for the recompute and each product)."""
+    kernel; per backward chunk of C columns 2 N d C for the recompute and
+    4 N d C for the launch holding both products)."""
     widths = chunk_widths(w, C)
     steps = len(fev)
     table = {}
     for kinds, evs in ((kinds_f, fev), (kinds_b, bev)):
-        chunk = {k: 0 for k in ("recompute", "product_dw", "product_dh")}
+        chunk = {k: 0 for k in CHUNK_PRODUCTS}
         for i, kind in enumerate(kinds):
             ms = sum(evs[s][2 * i].elapsed_time(evs[s][2 * i + 1])
                      for s in range(steps)) / steps
             if kind == "forward_tile":
                 fl = 2.0 * w.N * w.d * w.V
             elif kind in chunk:
-                fl = 2.0 * w.N * w.d * widths[chunk[kind]]
+                fl = (2.0 * CHUNK_PRODUCTS[kind] * w.N * w.d *
+                      widths[chunk[kind]])
                 chunk[kind] += 1
             else:
                 fl = 0.0

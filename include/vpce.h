@@ -234,9 +234,8 @@ typedef enum {
   VPCE_KERNEL_FORWARD_TILE = 1, /* logit tiles + online log-sum-exp */
   VPCE_KERNEL_MERGE = 2,        /* fold of shard/split partials, token NLL */
   VPCE_KERNEL_RECOMPUTE = 3,    /* backward: logit recompute, G chunk */
-  VPCE_KERNEL_PRODUCT_DW = 4,   /* backward: dW rows of a chunk = G^T H */
-  VPCE_KERNEL_PRODUCT_DH = 5,   /* backward: dH += G W_chunk */
-  VPCE_KERNEL_TRANSPOSE = 6,    /* operand layout copies */
+  VPCE_KERNEL_PRODUCTS = 4,     /* backward: a chunk's dW rows = G^T H and
+                                   dH += G W_chunk, one launch */
   VPCE_KERNEL_OTHER = 7         /* fills, loss mean, gradient scale */
 } vpce_kernel_kind_t;
 

@@ -277,8 +277,7 @@ def test_bench_kernel_table_from_event_pairs():
     assert bench.chunk_widths(w, 2) == [2, 2, 2, 1, 2, 1]
     assert bench.chunk_widths(w, 16384) == [4, 3, 3]
     kinds_f = ["other", "forward_tile", "merge", "other"]
-    kinds_b = ["other", "transpose"] + ["transpose", "recompute",
-                                        "product_dw", "product_dh"] * 3
+    kinds_b = ["other"] + ["recompute", "products"] * 3
 
     def evs(kinds, steps, dur):
         out = []
@@ -290,21 +289,21 @@ def test_bench_kernel_table_from_event_pairs():
         return out
 
     fev = evs(kinds_f, 2, lambda k, i: 4.0 if k == "forward_tile" else 0.01)
-    bev = evs(kinds_b, 2, lambda k, i: {"product_dw": 2.0,
-                                        "product_dh": 3.0}.get(k, 0.5))
+    bev = evs(kinds_b, 2, lambda k, i: {"products": 3.0}.get(k, 0.5))
     t = bench.kernel_table(w, kinds_f, fev, kinds_b, bev, 16384)
     # durations of step s are (1 + s) x base: the mean over 2 steps is 1.5 x
     assert t["forward_tile"]["launches_per_step"] == 1
     assert t["forward_tile"]["launch_ms"] == 6.0
     assert t["forward_tile"]["flops_per_launch"] == 2.0 * 1000 * 64 * 10
-    assert t["product_dh"]["launches_per_step"] == 3
-    assert t["product_dh"]["ms_per_step"] == 13.5
-    assert t["product_dh"]["flops_per_launch"] == 2.0 * 1000 * 64 * 10 / 3
-    assert t["transpose"]["launches_per_step"] == 4
-    assert "frac" not in t["transpose"]
+    assert t["products"]["launches_per_step"] == 3
+    assert t["products"]["ms_per_step"] == 13.5
+    # both products of chunks of 4, 3 and 3 columns: 4 N d (10 / 3) per launch
+    assert t["products"]["flops_per_launch"] == 4.0 * 1000 * 64 * 10 / 3
+    assert t["recompute"]["flops_per_launch"] == 2.0 * 1000 * 64 * 10 / 3
+    assert "frac" not in t["other"]
     assert t["other"]["launches_per_step"] == 3
     dom = max(t, key=lambda k: t[k]["ms_per_step"])
-    assert dom == "product_dh"
+    assert dom == "products"
 
 
 def test_bench_clock_sampler_without_the_tool(monkeypatch):

@@ -186,3 +186,48 @@ class _F64Rows:
     def __getitem__(self, idx):
         return (self.inp.H_f64(idx) if self.which == "H"
                 else self.inp.W_f64(idx))
+
+
+@pytest.mark.timeout(900)
+def test_v_sweep_at_full_size_keeps_the_workspace(vp):
+    """N=65536, d=7168, R=8 (the 1M-context slice's batch) at V = 32000,
+    64000, 128256 and 151936: the bytes requested from the allocator during
+    one forward + backward, less the inputs and outputs, are exactly the
+    workspace, the same for every V; sampled tokens' lse against the oracle
+    (their full logit rows)."""
+    N, d, R = 65536, 7168, 8
+    sizes = {}
+    for V in (32000, 64000, 128256, 151936):
+        w = WL.custom(N=N, d=d, V=V, R=R, w_std=0.03, labels="zipf",
+                      zipf_s=1.1, ignore_frac=0.02, name=f"vsweep_{V}")
+        say(f"case V-sweep N={N} d={d} V={V} R={R}: generating inputs")
+        inp = WL.make_inputs(w, 0)
+        H, W, lab = to_device(inp)
+        ws_bytes = vp.workspace_bytes(N, d, V, R, torch.bfloat16)
+        io_out = 4 * N + 4 + 4 * N * d + 4 * V * d
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_stats()["requested_bytes.all.current"]
+        torch.cuda.reset_peak_memory_stats()
+        loss, lse = vp.forward(H, W, lab, R)
+        dH, dW = vp.backward(H, W, lab, lse, None, R)
+        torch.cuda.synchronize()
+        peak = torch.cuda.memory_stats()["requested_bytes.all.peak"] - base
+        rows = np.random.default_rng(V).choice(N, size=16, replace=False)
+        glse = lse.cpu().numpy().astype(np.float64)[rows]
+        del loss, lse, dH, dW, H, W, lab
+        torch.cuda.empty_cache()
+        n_valid = int((inp.labels != WL.IGNORE_INDEX).sum())
+        rlse, _ = oracle.token_rows(inp.H_f64(rows), inp.W_f64(),
+                                    inp.labels[rows], n_valid)
+        e_lse = C.lse_err(glse, rlse)
+        # the inputs were allocated before the baseline; each call allocates
+        # its own workspace (the forward's is freed on return), so the peak
+        # above the baseline holds lse, loss, dH, dW and one workspace
+        extra = peak - io_out
+        say(f"V={V}: peak {peak} workspace {ws_bytes} extra {extra} "
+            f"lse_err {e_lse:.3e}")
+        sizes[V] = (ws_bytes, extra)
+        assert e_lse <= C.LSE_ABS
+    assert len({s[0] for s in sizes.values()}) == 1, sizes
+    for V, (ws_bytes, extra) in sizes.items():
+        assert extra == ws_bytes, (V, extra, ws_bytes)

@@ -84,11 +84,12 @@ def test_ragged_shapes(vp, case):
 
 
 def test_product_tile_switch_at_the_compute_unit_count(vp):
-    """The dW and dH products run on 128 x 256 tiles where 256 x 256 tiles
-    would be fewer than the device's compute units. With d = 2048 (8 column
-    tiles) these two shapes put dH just below and just above that count and
-    dW the other way round, so both layouts of both products meet the oracle,
-    with ragged row tails."""
+    """The dH product runs on 128 x 256 tiles where 256 x 256 tiles would be
+    fewer than the device's compute units (dW, whose operands are both read
+    K-outer, always on 256 x 256 tiles, in the same launch). With d = 2048 (8
+    column tiles) these two shapes put dH just below and just above that
+    count and the dW grid just at / below it, so both launch variants meet
+    the oracle, with ragged row tails."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rows = cus // 8                       # 256-row tiles for cus tiles
     cases = [

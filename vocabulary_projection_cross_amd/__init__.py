@@ -283,7 +283,7 @@ def backward(H: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
 # ---- timed variants (measurement) -----------------------------------------
 
 KERNEL_KINDS = {1: "forward_tile", 2: "merge", 3: "recompute",
-                4: "product_dw", 5: "product_dh", 6: "transpose", 7: "other"}
+                4: "products", 7: "other"}
 
 
 def _trace_args(events):

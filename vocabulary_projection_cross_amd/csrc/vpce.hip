@@ -614,15 +614,14 @@ struct ProdParams {
   int a_krows, b_krows;  // valid k-rows of K-outer operands
 };
 
+// One output tile of a product: tile idx (row-major in the grouped raster of
+// a.group output-row tiles) of out (+)= A . B^T. smem holds
+// RingOf<PL, T, TA, TB>::kBytes.
 template <typename T, typename PL, bool TA, bool TB>
-__global__ __launch_bounds__(PL::kThreads) __attribute__((amdgpu_waves_per_eu(PL::kWaves / 4, PL::kWaves / 4)))
-void prod_kernel(ProdParams a) {
+__device__ __forceinline__ void prod_tile(const ProdParams& a, int idx,
+                                          char* smem) {
   constexpr int kProdBandRows = ProdStage<PL>::kBandRows;
   constexpr int kProdPitch = ProdStage<PL>::kPitch;
-  __shared__ __attribute__((aligned(16))) char
-      smem[RingOf<PL, T, TA, TB>::kBytes];
-  const int total = a.TM * a.TN;
-  const int idx = xcd_remap(blockIdx.x, total);
   int tm, tn;
   grouped_tile(idx, a.TM, a.TN, a.group, tm, tn);
   const int64_t m0 = (int64_t)tm * PL::TM, n0 = (int64_t)tn * PL::TN;
@@ -696,6 +695,40 @@ void prod_kernel(ProdParams a) {
         __builtin_nontemporal_store(v[k], reinterpret_cast<f32x4_t*>(a.out + at[k]));
     lds_barrier();
   }
+}
+
+
+// The dW and dH products of one backward chunk in one launch: the workgroups
+// of each XCD (workgroup L runs on XCD L mod 8) take that XCD's share of the
+// dW tiles first and then its share of the dH tiles, each share a contiguous
+// range of its product's grouped raster. dW tiles (K = the batch's tokens)
+// are long; dH tiles (K = the chunk's columns) fill the compute units around
+// them, so a dW grid that is not a whole number of waves leaves no units
+// idle. dW: A = G and B = H, both K-outer; dH: A = G K-contiguous, B = the W
+// chunk K-outer, on DHL tiles.
+struct PairParams {
+  ProdParams dw, dh;
+  int n_dw, n_dh;  // tiles of each product
+};
+
+template <typename T, typename DHL>
+__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kWaves / 4, TL::kWaves / 4)))
+void prod_pair_kernel(PairParams a) {
+  static_assert(DHL::kThreads == TL::kThreads, "one block size");
+  constexpr int kDw = RingOf<TL, T, true, true>::kBytes;
+  constexpr int kDh = RingOf<DHL, T, false, true>::kBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kDw > kDh ? kDw : kDh];
+  const int total = a.n_dw + a.n_dh;
+  const int L = blockIdx.x, x = L & 7, k = L >> 3;
+  const int q = total >> 3, r = total & 7;
+  const int qw = a.n_dw >> 3, rw = a.n_dw & 7;
+  const int n_dw_x = qw + (x < rw ? 1 : 0);         // dW tiles of XCD x
+  const int dw0 = x * qw + (x < rw ? x : rw);       // its first dW tile
+  const int before = x * q + (x < r ? x : r);       // workgroups of XCDs < x
+  if (k < n_dw_x)
+    prod_tile<T, TL, true, true>(a.dw, dw0 + k, smem);
+  else
+    prod_tile<T, DHL, false, true>(a.dh, (before - dw0) + (k - n_dw_x), smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -894,22 +927,29 @@ int device_cus() {
   return cus;
 }
 
-// out (+)= A . B^T over pp.M output rows and pp.TN column tiles of 256: on
-// 256 x 256 tiles, or, when A is K-contiguous, on 128 x 256 tiles where the
-// former would give fewer tiles than the device has compute units. Sets pp.TM.
-template <typename T, bool TA, bool TB>
-int32_t launch_prod(ProdParams pp, int cus, int32_t kind, hipStream_t st,
-                    Trace* tr) {
-  const int64_t tiles = (pp.M + TL::TM - 1) / TL::TM * pp.TN;
-  if (!TA && cus > 0 && tiles < cus) {
-    pp.TM = (int)((pp.M + HL::TM - 1) / HL::TM);
-    VPCE_LAUNCH(kind, (prod_kernel<T, HL, false, TB>),
-                dim3((unsigned)(pp.TM * pp.TN)), dim3(HL::kThreads), pp);
-  } else {
-    pp.TM = (int)((pp.M + TL::TM - 1) / TL::TM);
-    VPCE_LAUNCH(kind, (prod_kernel<T, TL, TA, TB>),
-                dim3((unsigned)(pp.TM * pp.TN)), dim3(TL::kThreads), pp);
+// dW rows = G^T H and dH (+)= G W_chunk of one chunk in one launch (see
+// prod_pair_kernel). dH runs on 256 x 256 tiles, or on 128 x 256 tiles where
+// the former would give fewer tiles than the device has compute units. Sets
+// TM in both parameter sets.
+template <typename T>
+int32_t launch_products(ProdParams dw, ProdParams dh, bool with_dh, int cus,
+                        hipStream_t st, Trace* tr) {
+  dw.TM = (int)((dw.M + TL::TM - 1) / TL::TM);
+  PairParams pp{dw, dh, dw.TM * dw.TN, 0};
+  const int64_t dh_tiles = (dh.M + TL::TM - 1) / TL::TM * dh.TN;
+  const bool half = with_dh && cus > 0 && dh_tiles < cus;
+  if (with_dh) {
+    pp.dh.TM = (int)(half ? (dh.M + HL::TM - 1) / HL::TM
+                          : (dh.M + TL::TM - 1) / TL::TM);
+    pp.n_dh = pp.dh.TM * pp.dh.TN;
   }
+  const dim3 grid((unsigned)(pp.n_dw + pp.n_dh));
+  if (half)
+    VPCE_LAUNCH(VPCE_KERNEL_PRODUCTS, (prod_pair_kernel<T, HL>), grid,
+                dim3(TL::kThreads), pp);
+  else
+    VPCE_LAUNCH(VPCE_KERNEL_PRODUCTS, (prod_pair_kernel<T, TL>), grid,
+                dim3(TL::kThreads), pp);
   return VPCE_OK;
 }
 
@@ -945,24 +985,16 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
                   dim3((unsigned)(p.T * CT)), dim3(FL::kThreads), gp);
     }
     // dW rows of the chunk = G^T H: A = G (K-outer: row k = token, C_pad
-    // entries), B = H (K-outer: row k = token, d entries), K = N
-    {
-      ProdParams pp{G, cpad, ceff, H, p.d, p.d, p.N,
-                    dWspan + c0 * p.d, p.d, 0, TD, dW_acc ? 1 : 0, kGroupDW,
-                    (int)p.N, (int)p.N};
-      const int32_t rc =
-          launch_prod<T, true, true>(pp, cus, VPCE_KERNEL_PRODUCT_DW, st, tr);
-      if (rc != VPCE_OK) return rc;
-    }
+    // entries), B = H (K-outer: row k = token, d entries), K = N; and
     // dH (+)= G W_chunk: A = G [N x C_pad] (K-contiguous), B = W chunk
     // (K-outer: row k = vocabulary entry, d entries; rows past ceff read 0)
-    if (p.N > 0) {
-      ProdParams pp{G, cpad, p.N, Wc, p.d, p.d, cpad, dH, p.d, 0, TD,
-                    acc_h ? 1 : 0, kGroupDH, 0, (int)ceff};
-      const int32_t rc =
-          launch_prod<T, false, true>(pp, cus, VPCE_KERNEL_PRODUCT_DH, st, tr);
-      if (rc != VPCE_OK) return rc;
-    }
+    const ProdParams pw{G, cpad, ceff, H, p.d, p.d, p.N,
+                        dWspan + c0 * p.d, p.d, 0, TD, dW_acc ? 1 : 0,
+                        kGroupDW, (int)p.N, (int)p.N};
+    const ProdParams ph{G, cpad, p.N, Wc, p.d, p.d, cpad, dH, p.d, 0, TD,
+                        acc_h ? 1 : 0, kGroupDH, 0, (int)ceff};
+    const int32_t rc = launch_products<T>(pw, ph, p.N > 0, cus, st, tr);
+    if (rc != VPCE_OK) return rc;
     acc_h = true;
   }
   return VPCE_OK;
