@@ -433,15 +433,21 @@ __global__ void scale_from_totals_kernel(const double* totals,
   }
 }
 
-// The bf16 G tile leaves through LDS one wave column (FL::kWaveCols chunk
+// The bf16 G tile leaves through LDS one wave column (L::kWaveCols chunk
 // columns, the waves with one wn) at a time: each token row holds the
-// FL::kWaveCols columns, padded by 16 bytes so that the lanes writing 32
+// L::kWaveCols columns, padded by 16 bytes so that the lanes writing 32
 // different columns spread over the banks.
-constexpr int kGRowBytes = FL::kWaveCols * 2 + 16;
-constexpr int kGLds = kTile * kGRowBytes;
-constexpr int kRecLds =
-    RingOf<FL>::kBytes > kGLds ? RingOf<FL>::kBytes : kGLds;
-static_assert(FL::kWaveCols % 8 == 0, "16-byte row chunks");
+template <typename L>
+struct RecStage {
+  static constexpr int kGRowBytes = L::kWaveCols * 2 + 16;
+  static constexpr int kGLds = kTile * kGRowBytes;
+  static constexpr int kLds =
+      RingOf<L>::kBytes > kGLds ? RingOf<L>::kBytes : kGLds;
+  static_assert(L::kWaveCols % 8 == 0, "16-byte row chunks");
+};
+// The logit recompute runs on FL tiles (256 x 320), or on RL tiles
+// (256 x 256) where those leave fewer compute units idle in the last wave.
+using RL = Layout<256, 256, 4, 2>;
 
 struct GParams {
   const void* H;
@@ -464,11 +470,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 
-template <typename T>
-__global__ __launch_bounds__(FL::kThreads) __attribute__((amdgpu_waves_per_eu(kFwdWaves, kFwdWaves)))
+template <typename T, typename L>
+__global__ __launch_bounds__(L::kThreads) __attribute__((amdgpu_waves_per_eu(L::kWaves / 4, L::kWaves / 4)))
 void recompute_g_kernel(GParams a) {
+  constexpr int kGRowBytes = RecStage<L>::kGRowBytes;
   // The operand ring, reused after the mainloop to stage the bf16 G tile.
-  __shared__ __attribute__((aligned(16))) char smem[kRecLds];
+  __shared__ __attribute__((aligned(16))) char smem[RecStage<L>::kLds];
   __shared__ __attribute__((aligned(16))) int lab_s[kTile];
   __shared__ __attribute__((aligned(16))) float lse_s[kTile];
 
@@ -478,39 +485,39 @@ void recompute_g_kernel(GParams a) {
   grouped_tile(idx, a.T, a.CT, kGroupRec, it, ct);
   const int tid = threadIdx.x;
   const int64_t tok0 = (int64_t)it * kTile;
-  const int64_t c0 = (int64_t)ct * FL::TN;
+  const int64_t c0 = (int64_t)ct * L::TN;
   if (tid < kTile) {
     const int64_t tok = tok0 + tid;
     lab_s[tid] = tok < a.N ? label_code(a.labels[tok], a.ignore_index, a.V)
                            : kLabIgnored;
     lse_s[tid] = tok < a.N ? a.lse[tok] * kLog2e : 0.f;
   }
-  typename FL::Acc acc[FL::R][FL::C];
-  tile_mainloop<T, FL>(acc, reinterpret_cast<const T*>(a.H) + tok0 * a.d, a.d,
+  typename L::Acc acc[L::R][L::C];
+  tile_mainloop<T, L>(acc, reinterpret_cast<const T*>(a.H) + tok0 * a.d, a.d,
                        clamp_rows(a.N - tok0, kTile),
                        reinterpret_cast<const T*>(a.Wc) + c0 * a.d, a.d,
-                       clamp_rows(a.C_eff - c0, FL::TN), a.d, smem);
+                       clamp_rows(a.C_eff - c0, L::TN), a.d, smem);
   const float scale = a.scale[0];
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / FL::WN, wn = wave % FL::WN;
+  const int wm = wave / L::WN, wn = wave % L::WN;
   T* G = reinterpret_cast<T*>(a.G);
   // G packed to bf16 pairs (rows 2k, 2k + 1 of row group rq of accumulator
   // (i, jj) in gpk[i][jj][2rq + k]), or stored at once (fp32). Chunk columns
   // of this lane: ccol[jj] = c0 + wn * kWaveCols + col(jj) (< 2^31).
-  uint32_t gpk[FL::R][FL::C][FL::kAccRegs / 2];
-  int ccol[FL::C];
+  uint32_t gpk[L::R][L::C][L::kAccRegs / 2];
+  int ccol[L::C];
 #pragma unroll
-  for (int jj = 0; jj < FL::C; ++jj)
-    ccol[jj] = (int)c0 + wn * FL::kWaveCols + FL::col(jj, lane);
+  for (int jj = 0; jj < L::C; ++jj)
+    ccol[jj] = (int)c0 + wn * L::kWaveCols + L::col(jj, lane);
 #pragma unroll
-  for (int i = 0; i < FL::R; ++i) {
+  for (int i = 0; i < L::R; ++i) {
 #pragma unroll
-    for (int rq = 0; rq < FL::kRowGroups; ++rq) {
-      const int rowb = wm * FL::kWaveRows + FL::row_base(i, rq, lane);
+    for (int rq = 0; rq < L::kRowGroups; ++rq) {
+      const int rowb = wm * L::kWaveRows + L::row_base(i, rq, lane);
       const int4 labs = *reinterpret_cast<const int4*>(&lab_s[rowb]);
       const float4 l2 = *reinterpret_cast<const float4*>(&lse_s[rowb]);
 #pragma unroll
-      for (int jj = 0; jj < FL::C; ++jj) {
+      for (int jj = 0; jj < L::C; ++jj) {
         const int c = ccol[jj];
         const bool cvalid = c < a.C_eff;
         const int v = (int)a.cv0 + c;
@@ -545,22 +552,22 @@ void recompute_g_kernel(GParams a) {
   if constexpr (sizeof(T) == 2) {
     // The barriers order the LDS staging only; the G stores stay in flight
     // across them and past the end of the workgroup.
-    constexpr int kRowChunks = FL::kWaveCols * 2 / 16;  // per G row (one pass)
+    constexpr int kRowChunks = L::kWaveCols * 2 / 16;  // per G row (one pass)
 #pragma unroll 1
-    for (int pass = 0; pass < FL::WN; ++pass) {
-      const int64_t cp0 = c0 + pass * FL::kWaveCols;  // first column of the pass
+    for (int pass = 0; pass < L::WN; ++pass) {
+      const int64_t cp0 = c0 + pass * L::kWaveCols;  // first column of the pass
       // G rows: the waves of this column write their columns row-major, then
       // every lane stores 16-byte chunks of the rows, coalesced.
       if (wn == pass) {
 #pragma unroll
-        for (int jj = 0; jj < FL::C; ++jj) {
-          const int cl = FL::col(jj, lane);
+        for (int jj = 0; jj < L::C; ++jj) {
+          const int cl = L::col(jj, lane);
 #pragma unroll
-          for (int i = 0; i < FL::R; ++i)
+          for (int i = 0; i < L::R; ++i)
 #pragma unroll
-            for (int rr = 0; rr < FL::kAccRegs; ++rr) {
-              const int row = wm * FL::kWaveRows +
-                              FL::row_base(i, rr >> 2, lane) + (rr & 3);
+            for (int rr = 0; rr < L::kAccRegs; ++rr) {
+              const int row = wm * L::kWaveRows +
+                              L::row_base(i, rr >> 2, lane) + (rr & 3);
               *reinterpret_cast<uint16_t*>(smem + row * kGRowBytes + cl * 2) =
                   (uint16_t)(gpk[i][jj][rr >> 1] >> (16 * (rr & 1)));
             }
@@ -568,7 +575,7 @@ void recompute_g_kernel(GParams a) {
       }
       lds_barrier();
 #pragma unroll 4
-      for (int id = tid; id < kTile * kRowChunks; id += FL::kThreads) {
+      for (int id = tid; id < kTile * kRowChunks; id += L::kThreads) {
         const int row = id / kRowChunks, u = id % kRowChunks;
         const int64_t tok = tok0 + row;
         const int64_t cc = cp0 + 8 * u;
@@ -750,14 +757,34 @@ struct Plan {
   size_t bytes;
 };
 
+// The most vocabulary splits per shard a forward may use: enough workgroups
+// to cover 256 compute units twice, at most kMaxSplits. It sizes the
+// per-token partial states in the workspace, so it never depends on V.
 int splits_for(int64_t T, int R) {
-  // enough workgroups to cover the 256 compute units twice, never
-  // depending on V
   const int64_t want = 512;
   int64_t s = (want + T * R - 1) / (T * R);
   if (s < 1) s = 1;
   if (s > kMaxSplits) s = kMaxSplits;
   return (int)s;
+}
+
+// The splits a forward runs with, at most s_cap: the fewest whose makespan --
+// waves of T x R x S workgroups (one per compute unit) times the most
+// vocabulary tiles one split of the widest shard holds -- is the smallest.
+int run_splits(int64_t T, int R, int s_cap, int64_t widest, int cus) {
+  const int64_t units = cus > 0 ? cus : 256;
+  const int64_t Q = (widest + FL::TN - 1) / FL::TN;
+  int best = 1;
+  int64_t best_span = -1;
+  for (int s = 1; s <= s_cap; ++s) {
+    const int64_t waves = (T * R * s + units - 1) / units;
+    const int64_t span = waves * ((Q + s - 1) / s);
+    if (best_span < 0 || span < best_span) {
+      best_span = span;
+      best = s;
+    }
+  }
+  return best;
 }
 
 int32_t check_shape(int64_t N, int64_t d, int64_t V, int32_t R, int32_t dt) {
@@ -890,6 +917,16 @@ inline int32_t trace_end(Trace* t, int32_t kind, hipStream_t st) {
     if (trace_end(tr, KIND, st) != VPCE_OK) return VPCE_ERR_HIP;         \
   } while (0)
 
+// Compute units of the current device (0 if the runtime cannot say).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
 template <typename T>
 int32_t run_forward(const Plan& p, const void* H, const void* W,
                     const int64_t* labels, int64_t ignore_index, float* loss,
@@ -903,13 +940,15 @@ int32_t run_forward(const Plan& p, const void* H, const void* W,
   if (p.N > 0) {
     VPCE_LAUNCH(VPCE_KERNEL_OTHER, fill_kernel,
                 dim3((unsigned)((p.N + 255) / 256)), dim3(256), tgt, p.N, NAN);
-    FwdParams fp{H, W, labels, p.N, p.d, p.V, ignore_index, p.R, p.S, p.T,
+    const int S = run_splits(p.T, p.R, p.S, Shards{p.V, p.R}.width(0),
+                             device_cus());
+    FwdParams fp{H, W, labels, p.N, p.d, p.V, ignore_index, p.R, S, p.T,
                  pm, ps, tgt, 0, p.V};
-    const unsigned grid = (unsigned)((int64_t)p.T * p.R * p.S);
+    const unsigned grid = (unsigned)((int64_t)p.T * p.R * S);
     VPCE_LAUNCH(VPCE_KERNEL_FORWARD_TILE, fwd_lse_kernel<T>, dim3(grid),
                 dim3(FL::kThreads), fp);
     VPCE_LAUNCH(VPCE_KERNEL_MERGE, merge_kernel, dim3((unsigned)p.nb),
-                dim3(256), pm, ps, tgt, labels, p.N, p.R * p.S, ignore_index,
+                dim3(256), pm, ps, tgt, labels, p.N, p.R * S, ignore_index,
                 lse, bsum, bcnt);
   }
   VPCE_LAUNCH(VPCE_KERNEL_OTHER, loss_kernel, dim3(1), dim3(256), bsum, bcnt,
@@ -917,15 +956,6 @@ int32_t run_forward(const Plan& p, const void* H, const void* W,
   return VPCE_OK;
 }
 
-// Compute units of the current device (0 if the runtime cannot say).
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                            dev) != hipSuccess)
-    return 0;
-  return cus;
-}
 
 // dW rows = G^T H and dH (+)= G W_chunk of one chunk in one launch (see
 // prod_pair_kernel). dH runs on 256 x 256 tiles, or on 128 x 256 tiles where
@@ -977,12 +1007,26 @@ int32_t backward_span(const Plan& p, const void* H, const void* Wspan,
     const int64_t cpad = (ceff + 63) / 64 * 64;
     const int64_t cv0 = v_first + c0;
     const T* Wc = reinterpret_cast<const T*>(Wspan) + c0 * p.d;
-    const int CT = (int)((cpad + FL::TN - 1) / FL::TN);
     if (p.N > 0) {
+      // 256 x 256 recompute tiles where their last wave leaves clearly fewer
+      // compute units idle: the makespan in column-units (waves of one
+      // workgroup per unit, times the tile width) at least 10% below that
+      // of 256 x 320 tiles, which move fewer operand bytes per flop
+      const int64_t units = cus > 0 ? cus : 256;
+      const int64_t ct_w = (cpad + FL::TN - 1) / FL::TN;
+      const int64_t ct_n = (cpad + RL::TN - 1) / RL::TN;
+      const int64_t span_w = (p.T * ct_w + units - 1) / units * FL::TN;
+      const int64_t span_n = (p.T * ct_n + units - 1) / units * RL::TN;
+      const bool narrow = 10 * span_n < 9 * span_w;
+      const int CT = (int)(narrow ? ct_n : ct_w);
       GParams gp{H, Wc, labels, lse, scale, p.N, p.d, V_lab,
                  ignore_index, cv0, ceff, cpad, p.T, CT, G};
-      VPCE_LAUNCH(VPCE_KERNEL_RECOMPUTE, recompute_g_kernel<T>,
-                  dim3((unsigned)(p.T * CT)), dim3(FL::kThreads), gp);
+      if (narrow)
+        VPCE_LAUNCH(VPCE_KERNEL_RECOMPUTE, (recompute_g_kernel<T, RL>),
+                    dim3((unsigned)(p.T * CT)), dim3(RL::kThreads), gp);
+      else
+        VPCE_LAUNCH(VPCE_KERNEL_RECOMPUTE, (recompute_g_kernel<T, FL>),
+                    dim3((unsigned)(p.T * CT)), dim3(FL::kThreads), gp);
     }
     // dW rows of the chunk = G^T H: A = G (K-outer: row k = token, C_pad
     // entries), B = H (K-outer: row k = token, d entries), K = N; and
@@ -1030,13 +1074,14 @@ int32_t run_shard_fold(const Plan& p, const void* H, const void* Wshard,
   if (p.N == 0) return VPCE_OK;
   float* pm = reinterpret_cast<float*>(ws + p.o_pm);
   float* ps = reinterpret_cast<float*>(ws + p.o_ps);
-  FwdParams fp{H, Wshard, labels, p.N, p.d, p.V, ignore_index, 1, p.S, p.T,
+  const int S = run_splits(p.T, 1, p.S, p.V, device_cus());
+  FwdParams fp{H, Wshard, labels, p.N, p.d, p.V, ignore_index, 1, S, p.T,
                pm, ps, state + 2 * p.N, v_begin, V_lab};
-  hipLaunchKernelGGL(fwd_lse_kernel<T>, dim3((unsigned)((int64_t)p.T * p.S)),
+  hipLaunchKernelGGL(fwd_lse_kernel<T>, dim3((unsigned)((int64_t)p.T * S)),
                      dim3(FL::kThreads), 0, st, fp);
   VPCE_LAUNCH_CHECK();
   hipLaunchKernelGGL(fold_state_kernel, dim3((unsigned)((p.N + 255) / 256)),
-                     dim3(256), 0, st, pm, ps, p.N, p.S, state, state + p.N);
+                     dim3(256), 0, st, pm, ps, p.N, S, state, state + p.N);
   VPCE_LAUNCH_CHECK();
   return VPCE_OK;
 }
