@@ -8,6 +8,7 @@ resident in HBM. Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-seconds S] [--input-cache DIR]
+                    [--no-clock]
     python bench.py --copy-calibration   # plain 1 GiB device copies, for
                                          # scaling HBM traffic counters
 
@@ -155,8 +156,9 @@ class ClockSampler:
     (a child process) while the timed steps run; reports the median of the
     per-sample XCD means, or None where the tool is missing or fails."""
 
-    def __init__(self):
+    def __init__(self, enabled=True):
         import threading
+        self.enabled = enabled
         self.samples = []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
@@ -178,12 +180,14 @@ class ClockSampler:
             self._stop.wait(0.2)
 
     def __enter__(self):
-        self._thread.start()
+        if self.enabled:
+            self._thread.start()
         return self
 
     def __exit__(self, *exc):
         self._stop.set()
-        self._thread.join(timeout=15)
+        if self.enabled:
+            self._thread.join(timeout=15)
 
     def median(self):
         if not self.samples:
@@ -276,6 +280,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--input-cache", default=None)
     ap.add_argument("--copy-calibration", action="store_true")
+    # no shader-clock sampling (it starts amd-smi child processes, which a
+    # profiler that has already initialised the GPU may not allow)
+    ap.add_argument("--no-clock", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -350,7 +357,7 @@ def main():
     kinds_f = kinds_b = None
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
+    with ClockSampler(enabled=not args.no_clock) as clock:
         wall0 = time.perf_counter()
         t_all0.record(stream)
         for k in range(args.steps):
