@@ -8,7 +8,7 @@ resident in HBM. Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-seconds S] [--input-cache DIR]
-                    [--no-clock]
+                    [--no-clock] [--chunk-cols C]
     python bench.py --copy-calibration   # plain 1 GiB device copies, for
                                          # scaling HBM traffic counters
 
@@ -136,9 +136,10 @@ def kernel_table(w, kinds_f, fev, kinds_b, bev, C):
     return table
 
 
-def traffic_record(workload: str, kernel: str):
+def traffic_record(workload: str, kernel: str, chunk_cols=None):
     """Measured HBM bytes per launch of `kernel`, if the stored counter
-    summary was taken from the device code built now."""
+    summary was taken from the device code built now (and, for the backward
+    kernels, at the same chunk width)."""
     stem = kernel.split(" ")[0]
     path = os.path.join(ROOT, "profiles",
                         f"{stem}_traffic_{workload}.json")
@@ -147,6 +148,9 @@ def traffic_record(workload: str, kernel: str):
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_code_hash") != kernel_code_hash():
+        return None
+    if chunk_cols is not None and rec.get("chunk_cols", chunk_cols) != \
+            chunk_cols:
         return None
     return rec
 
@@ -280,6 +284,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--input-cache", default=None)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--chunk-cols", type=int, default=None)
     # no shader-clock sampling (it starts amd-smi child processes, which a
     # profiler that has already initialised the GPU may not allow)
     ap.add_argument("--no-clock", action="store_true")
@@ -314,8 +319,13 @@ def main():
         W = torch.from_numpy(np.ascontiguousarray(inp.W)).to(dev)
     lab = torch.from_numpy(np.ascontiguousarray(inp.labels)).to(dev)
     dloss = torch.ones(1, dtype=torch.float32, device=dev)
-    ws = torch.empty(vp.workspace_bytes(w.N, w.d, w.V, w.R, H.dtype),
+    # the workspace at the widest backward chunk, or at --chunk-cols (the
+    # planner's narrower chunks: less memory, more dH read-modify-writes)
+    ws = torch.empty(vp.workspace_bytes(w.N, w.d, w.V, w.R, H.dtype,
+                                        chunk_cols=args.chunk_cols),
                      dtype=torch.uint8, device=dev)
+    chunk = args.chunk_cols or vp.plan(w.N, w.d, w.V, w.R, 1 << 62,
+                                       H.dtype)["chunk_cols"]
     torch.cuda.synchronize()
     in_bytes = sum(t.numel() * t.element_size() for t in (H, W, lab))
 
@@ -374,9 +384,7 @@ def main():
     total_ms = t_all0.elapsed_time(t_all1)
     fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
     bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
-    kernels = kernel_table(w, kinds_f, fev, kinds_b, bev,
-                           vp.plan(w.N, w.d, w.V, w.R, 1 << 62,
-                                   H.dtype)["chunk_cols"])
+    kernels = kernel_table(w, kinds_f, fev, kinds_b, bev, chunk)
     out_bytes = sum(t.numel() * t.element_size() for t in (loss, lse, dH, dW))
     # peak device bytes of one step, the previous outputs released
     del loss, lse, dH, dW
@@ -386,7 +394,8 @@ def main():
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated()
     requested_peak = torch.cuda.memory_stats()["requested_bytes.all.peak"]
-    planned = vp.plan(w.N, w.d, w.V, w.R, 1 << 62, H.dtype)
+    fixed = in_bytes + out_bytes
+    planned = vp.plan(w.N, w.d, w.V, w.R, fixed + ws.numel(), H.dtype)
     ms = total_ms / args.steps
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -395,7 +404,7 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
     dom_tf = dk["flops_per_launch"] / (dk["launch_ms"] * 1e-3) / 1e12
-    trec = traffic_record(w.name, dk["kernel"])
+    trec = traffic_record(w.name, dk["kernel"], chunk)
     traffic = None
     if trec is not None:
         traffic = int(trec["hbm_bytes_per_launch"])
@@ -416,7 +425,8 @@ def main():
                  "Zipf(1.1) labels over a permuted vocabulary, 2% ignored)"
                  if w.name == HEADLINE else "synthetic (seeded)"),
         "config": {"workload": w.name, "N": w.N, "d": w.d, "V": w.V,
-                   "R": w.R, "global_batch": w.N, "parallelism": "none"},
+                   "R": w.R, "chunk_cols": chunk, "global_batch": w.N,
+                   "parallelism": "none"},
         "tflops": tflops,
         "pct_mfma_peak": 100.0 * tflops / peak_tf,
         "fwd_ms": float(np.mean(fwd_ms)),

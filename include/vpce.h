@@ -75,7 +75,7 @@ typedef enum {
 
 /*
  * Bytes of device workspace that one buffer serving both vpce_forward and
- * vpce_backward needs for this shape at the widest backward chunk (16384
+ * vpce_backward needs for this shape at the widest backward chunk (8192
  * vocabulary columns). Pure host function (no GPU call). The result does not
  * depend on V: the forward keeps per-token partial states for R shards times
  * a fixed number of vocabulary splits, the backward a fixed-width chunk of
@@ -89,7 +89,7 @@ size_t vpce_workspace_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
 
 /*
  * As vpce_workspace_bytes, for a backward chunk of chunk_cols vocabulary
- * columns (a multiple of 256 in [256, 16384]; 0 is returned otherwise). The
+ * columns (a multiple of 256 in [256, 8192]; 0 is returned otherwise). The
  * backward chunk is the memory that stands in for the logit strip of section
  * 3.2: the backward's workspace is its gradient chunk G [N x C] (bf16 for
  * bf16 inputs, fp32 for fp32), one N x C strip. Narrower chunks cost more

@@ -133,12 +133,12 @@ def _caller_bytes(N, d, V, esz):
                                      (4096, 2048, 32000, 4), (300, 136, 1000, 3)])
 def test_chunk_workspace_grows_with_the_chunk(lib, N, d, V, R):
     full = lib.vpce_workspace_bytes(N, d, V, R, 0)
-    assert lib.vpce_workspace_bytes_chunk(N, d, V, R, 0, 16384) == full
+    assert lib.vpce_workspace_bytes_chunk(N, d, V, R, 0, 8192) == full
     sizes = [lib.vpce_workspace_bytes_chunk(N, d, V, R, 0, c)
-             for c in range(256, 16385, 256)]
+             for c in range(256, 8193, 256)]
     assert all(a <= b for a, b in zip(sizes, sizes[1:]))
     assert sizes[0] < sizes[-1]
-    for bad in (0, 128, 255, 300, 16640, -256):
+    for bad in (0, 128, 255, 300, 8448, 16384, -256):
         assert lib.vpce_workspace_bytes_chunk(N, d, V, R, 0, bad) == 0
 
 
@@ -150,7 +150,7 @@ def test_planner_picks_the_widest_chunk_that_fits(N, d, V, R, dt):
     dtype = torch.bfloat16 if dt == 0 else torch.float32
     esz = 2 if dt == 0 else 4
     fixed = _caller_bytes(N, d, V, esz)
-    for C in (256, 4096, 12800, 16384):
+    for C in (256, 4096, 6400, 8192):
         ws = vp.workspace_bytes(N, d, V, R, dtype, chunk_cols=C)
         exact = vp.plan(N, d, V, R, fixed + ws, dtype)
         assert exact == {"chunk_cols": C, "workspace_bytes": ws,
@@ -160,7 +160,7 @@ def test_planner_picks_the_widest_chunk_that_fits(N, d, V, R, dt):
             assert below["chunk_cols"] < C
             assert below["peak_bytes"] <= fixed + ws - 1
     roomy = vp.plan(N, d, V, R, 1 << 50, dtype)
-    assert roomy["chunk_cols"] == 16384
+    assert roomy["chunk_cols"] == 8192
     assert roomy["workspace_bytes"] == vp.workspace_bytes(N, d, V, R, dtype)
     ws256 = vp.workspace_bytes(N, d, V, R, dtype, chunk_cols=256)
     with pytest.raises(vp.VPCEError, match="status 5"):
@@ -253,6 +253,10 @@ def test_bench_traffic_record_goes_stale_with_the_device_code(tmp_path,
     k = "prod_kernel (dH += G W)"
     assert bench.traffic_record("w", k)["hbm_bytes_per_launch"] == 123
     assert bench.traffic_record("w", "fwd_lse_kernel") is None
+    rec["chunk_cols"] = 8192
+    (prof / "prod_kernel_traffic_w.json").write_text(json.dumps(rec))
+    assert bench.traffic_record("w", k, 8192)["hbm_bytes_per_launch"] == 123
+    assert bench.traffic_record("w", k, 4096) is None
     rec["kernel_code_hash"] = "0" * 16
     (prof / "prod_kernel_traffic_w.json").write_text(json.dumps(rec))
     assert bench.traffic_record("w", k) is None

@@ -66,7 +66,7 @@ RAGGED = [
     (64, 64, 33, 33, "f32"),
     (700, 520, 4500, 1, "bf16"),
     (300, 64, 40000, 1, "bf16"),   # one shard over three backward chunks
-                                   # (16384 + 16384 + ragged 7232 columns)
+                                   # (4 x 8192 + ragged 7232 columns)
     # shard widths at, above and below the 320-column vocabulary tile
     (260, 64, 640, 2, "bf16"),     # 320 + 320: whole tiles
     (300, 136, 963, 3, "bf16"),    # 321 each: a full tile and a 1-column one

@@ -149,7 +149,7 @@ def workspace_bytes(N: int, d: int, V: int, R: int,
                     chunk_cols: Optional[int] = None) -> int:
     """Workspace bytes for forward + backward (0 for invalid arguments): at
     the widest backward chunk, or at chunk_cols (a multiple of 256 in
-    [256, 16384])."""
+    [256, 8192])."""
     if chunk_cols is None:
         return int(_load().vpce_workspace_bytes(N, d, V, R,
                                                 _dtype_code(dtype)))

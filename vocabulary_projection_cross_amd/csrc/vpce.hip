@@ -42,12 +42,14 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Backward chunk width C: at most 64 column tiles, so the dW grid
-// (64 x ceil(d/256) tiles) fills whole waves of 256 workgroups for d a
-// multiple of 1024, and the fp32 read-modify-write of dH happens once per
-// 16384 vocabulary rows. A smaller workspace gets the widest multiple of
-// kChunkStep that fits.
-constexpr int kChunkCols = 16384;
+// Backward chunk width C: at most 32 column tiles of the dW product. Measured
+// on the workloads of 16384 to 131072 tokens, 8192 columns are as fast as
+// 16384 (the 1M-context slice) or faster (2% on the stress workload, whose
+// 21706-column shards then split 8192 + 8192 + 5322) at half the workspace;
+// 4096 is 2% slower on the 1M-context slice (twice the fp32 read-modify-write
+// passes of dH). A smaller workspace gets the widest multiple of kChunkStep
+// that fits.
+constexpr int kChunkCols = 8192;
 constexpr int kChunkStep = 256;
 constexpr int kMaxSplits = 16;
 constexpr int64_t kMaxTokens = 2000000;
