@@ -346,3 +346,42 @@ def test_seeded_random_shapes(vp):
         w = WL.custom(N=N, d=d, V=V, R=R, dtype=dt, w_std=w_std,
                       ignore_frac=ign, name=f"random{case}")
         full_check(vp, w, seed=case, dloss=dloss)
+
+
+def test_traced_calls_match_and_bracket_every_launch(vp):
+    """vpce_forward_traced / vpce_backward_traced: the same outputs as the
+    untraced calls (bitwise), one event pair per kernel launch with its kind
+    in launch order (forward: fill, tile kernel, merge, loss; backward: the
+    gradient scale, then per chunk the recompute and the product launch),
+    and every pair's elapsed time is non-negative."""
+    N, d, V, R = 700, 136, 4500, 3      # shards 1500: one chunk each
+    w = WL.custom(N=N, d=d, V=V, R=R, w_std=0.3, ignore_frac=0.05,
+                  name="traced")
+    inp = WL.make_inputs(w, 17)
+    H, W, lab = to_device(inp)
+    say(f"case traced calls N={N} d={d} V={V} R={R}")
+    loss0, lse0 = vp.forward(H, W, lab, R)
+    dH0, dW0 = vp.backward(H, W, lab, lse0, None, R)
+
+    def events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for e in evs:
+            e.record()
+        return evs
+
+    fe, be = events(8), events(16)
+    loss, lse, kf, nf = vp.forward_traced(H, W, lab, R, fe)
+    dH, dW, kb, nb = vp.backward_traced(H, W, lab, lse, None, R, be)
+    torch.cuda.synchronize()
+    assert kf == ["other", "forward_tile", "merge", "other"] and nf == 4
+    assert kb == ["other"] + ["recompute", "products"] * R and nb == 1 + 2 * R
+    for evs, n in ((fe, nf), (be, nb)):
+        for i in range(n):
+            assert evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0.0
+    assert torch.equal(loss, loss0) and torch.equal(lse, lse0)
+    assert torch.equal(dH, dH0) and torch.equal(dW, dW0)
+    # fewer event pairs than launches: the rest are counted, not bracketed
+    few = events(2)
+    _, _, kb2, nb2 = vp.backward_traced(H, W, lab, lse, None, R, few)
+    torch.cuda.synchronize()
+    assert kb2 == ["other", "recompute"] and nb2 == nb
