@@ -136,6 +136,9 @@ int32_t vpce_plan(int64_t N, int64_t d, int64_t V, int32_t R, int32_t dtype,
  *                                 vpce_workspace_bytes_chunk(..., 256) holds
  *   stream                        hipStream_t to enqueue on
  * Returns VPCE_OK or an error status (nothing enqueued on argument errors).
+ * Results are bitwise reproducible for a fixed shape on one device model: the
+ * number of vocabulary splits per shard follows the device's compute-unit
+ * count, and it sets the order in which the fp32 partial states are merged.
  */
 int32_t vpce_forward(const void* H, const void* W, const int64_t* labels,
                      int64_t N, int64_t d, int64_t V, int32_t R,
@@ -199,8 +202,10 @@ size_t vpce_forward_noalloc_bytes(int64_t N, int64_t d, int64_t V, int32_t R,
  *                                 VPCE_ERR_WORKSPACE)
  * with G_ij = valid_i * (exp(z_ij - lse_i) - [j == y_i]). The token count
  * n_valid is recounted from labels. Rows of dH for ignored tokens are exactly
- * zero. Results are bitwise reproducible for a fixed shape and workspace size
- * (no atomics); the chunk width changes only the fp32 summation order of dH.
+ * zero. Results are bitwise reproducible for a fixed shape, lse and
+ * workspace size (no atomics; the tile shapes chosen from the device's
+ * compute-unit count change no summation order); the chunk width changes only
+ * the fp32 summation order of dH.
  */
 int32_t vpce_backward(const void* H, const void* W, const int64_t* labels,
                       const float* lse, const float* dloss, int64_t N,

@@ -292,10 +292,10 @@ __device__ __forceinline__ void copy16_to_lds(uint32_t lds_addr,
 
 // A byte offset that every buffer resource here rejects (loads read zero).
 // Resources span less than 2^31 bytes, and a block offset added to it (at
-// most 256 rows of an operand pitch; the longest pitch is a row of an fp32
-// transposed H, 4 * N_pad bytes, which the library's token limit keeps below
-// 8.0e6, so under 2.05e9) leaves it below 2^32, so it stays rejected. The
-// library checks that bound against its shape limits at compile time.
+// most 256 rows of a K-contiguous operand's pitch, a row of fp32 H or W:
+// 4 d bytes) leaves it below 2^32, so it stays rejected. The library checks
+// that bound against its largest d at compile time. K-outer operands never
+// take this offset: their stages past K get an empty resource instead.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int64_t kMaxBlockOffsetRows = 256;
 
