@@ -389,11 +389,20 @@ def main():
     # peak device bytes of one step, the previous outputs released
     del loss, lse, dH, dW
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
+    # device-level cross-check: the memory the device reports in use grows by
+    # no more than torch's allocator reserved (the HIP runtime may hand back
+    # memory it kept from earlier frees, so it can grow by less), so the
+    # library allocated nothing of its own during the step
+    free0 = torch.cuda.mem_get_info(dev)[0]
+    reserved0 = torch.cuda.memory_reserved(dev)
     loss, lse, dH, dW = step()
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated()
     requested_peak = torch.cuda.memory_stats()["requested_bytes.all.peak"]
+    device_used_delta = free0 - torch.cuda.mem_get_info(dev)[0]
+    reserved_delta = torch.cuda.memory_reserved(dev) - reserved0
     fixed = in_bytes + out_bytes
     planned = vp.plan(w.N, w.d, w.V, w.R, fixed + ws.numel(), H.dtype)
     ms = total_ms / args.steps
@@ -442,6 +451,11 @@ def main():
         # block rounding) and the planner's prediction made before launch;
         # they differ by the 4-byte upstream-gradient scalar
         "requested_peak_bytes": int(requested_peak),
+        # hipMemGetInfo's used-bytes growth over the step and the growth of
+        # torch's reserved pool; the first exceeds the second only if
+        # something outside torch allocated device memory
+        "device_used_delta_bytes": int(device_used_delta),
+        "torch_reserved_delta_bytes": int(reserved_delta),
         "planned_peak_bytes": planned["peak_bytes"],
         "roofline": {"bound": "mfma", "kernel": dk["kernel"],
                      "achieved": dom_tf, "peak": peak_tf, "unit": "TFLOP/s",
