@@ -584,7 +584,11 @@ void recompute_g_kernel(GParams a) {
         if (tok < a.N && cc < a.C_pad) {
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
               smem + row * kGRowBytes + u * 16);
-          *reinterpret_cast<u32x4_t*>(G + tok * a.C_pad + cc) = v;
+          // non-temporal: the chunk (1 GB on the 65536-token batch) is
+          // re-read only by the next launch, and keeping it out of the
+          // caches measured 0.4-0.9% faster per step than plain stores
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<u32x4_t*>(G + tok * a.C_pad + cc));
         }
       }
       lds_barrier();
