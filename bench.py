@@ -470,7 +470,11 @@ def main():
                      "kernels": kernels,
                      # the published peak assumes a 2400 MHz shader clock;
                      # this is the clock the chip held during the timed steps
-                     "sclk_mhz_timed": clock.median(),
+                     # (null when the timed steps last under 2 s: the
+                     # sampler, a child process polling every 0.2 s, then
+                     # mostly sees the idle clock before and after them)
+                     "sclk_mhz_timed": (clock.median() if total_ms >= 2000.0
+                                        else None),
                      "sclk_samples": len(clock.samples)},
         "cpu_baseline": None,
     }
